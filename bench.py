@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of one packed engine step (append + paged attention) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--gpus 1]
+
+A step is pkv_append of the step's new K/V rows followed by pkv_attention over
+the whole batch, on synthetic N(0,1) data already resident in HBM.  The
+default workload is the 128-sequence large decode batch (contexts uniform in
+[4096, 32768], 64 query / 8 kv heads, head_dim 128, page size 16, bf16): its
+9.7 GB of keys and values cannot stay in the 256 MB Infinity Cache, so back to
+back steps read HBM.  One JSON line is printed:
+
+  value      decode KV-read GB/s = valid K/V bytes of the step / step time
+  roofline   the decode pass (split-key partial + merge kernels) against the
+             8 TB/s HBM peak, timed with HIP events on the launch stream
+  cpu_baseline  the float64 oracle on the host cores over a bounded sample
+  extra      the mixed chunked-prefill step: packed-step tokens/s and the
+             prefill kernel's MFMA utilisation against 2.5 PFLOP/s dense bf16
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_kv_attention_03_amd as pkv  # noqa: E402
+from paged_kv_attention_03_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak, published
+METRIC = "decode KV-read GB/s (% HBM peak) + packed-step tokens/s; prefill MFMA util"
+KERNEL_SOURCES = ["decode.hpp", "pkv_device.hpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kv_bytes(st) -> int:
+    """Valid K+V bytes a step reads: sum over sequences of (keys - kv_start)
+    * 2 (K and V) * Hkv * D * element size."""
+    e = 2 if st.dtype == torch.bfloat16 else 4
+    return int(sum(st.real_lens) * 2 * st.num_kv_heads * st.head_dim * e)
+
+
+def prefill_flops(st) -> float:
+    """QK^T and PV multiply-adds (2 flops each) over every visible
+    (query token, key) pair of the prefill sequences, for all query heads."""
+    pairs = 0
+    for L, n in zip(st.real_lens, st.q_lens):
+        if n >= 2:
+            pairs += sum(L - n + i + 1 for i in range(n))
+    return 4.0 * st.head_dim * st.num_q_heads * pairs
+
+
+class Step:
+    """Resident device state of one workload: pools, metadata, the step's
+    rows, q, out and workspace."""
+
+    def __init__(self, st, gen_device="cuda"):
+        self.st = st
+        self.kp, self.vp = st.new_pool("cuda", poison=False)
+        k, v, s = st.rows("fill", "cuda", gen_device=gen_device)
+        if k.shape[0]:
+            pkv.pkv_append(k, v, self.kp, self.vp, s)
+        del k, v, s
+        self.k_new, self.v_new, self.slots = st.rows("step", "cuda", gen_device=gen_device)
+        md = st.metadata("cuda")
+        self.bt, self.sl, self.qsl, self.ks = (md["block_tables"], md["seq_lens"],
+                                               md["query_start_loc"], md["kv_start"])
+        self.q = st.make_q("cuda", gen_device=gen_device)
+        self.out = torch.empty_like(self.q)
+        need = pkv.pkv_attention_workspace_size(st.num_seqs, st.total_q, st.max_seqlen_q,
+                                                st.max_seqlen_k, st.num_q_heads,
+                                                st.num_kv_heads, st.head_dim, 16, st.dtype)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def append(self):
+        pkv.pkv_append(self.k_new, self.v_new, self.kp, self.vp, self.slots)
+
+    def attention(self):
+        st = self.st
+        pkv.pkv_attention(self.q, self.kp, self.vp, self.bt, self.sl, self.qsl, st.scale,
+                          max_seqlen_q=st.max_seqlen_q, max_seqlen_k=st.max_seqlen_k,
+                          kv_start=self.ks, out=self.out, workspace=self.ws)
+
+
+def time_steps(step: Step, steps: int, warmup: int, flush_bytes: int = 0):
+    """Whole-step wall time over ``steps`` steps, and the attention call's
+    average duration from HIP events recorded on the launch stream."""
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    for _ in range(warmup):
+        step.append()
+        step.attention()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    if flush is None:
+        t0 = time.perf_counter()
+        for a, b in ev:
+            step.append()
+            a.record()
+            step.attention()
+            b.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+    else:
+        # caches are cleared before every step; the wall time then excludes the
+        # clearing by summing per-step event pairs around append + attention
+        wall_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+        for (a, b), (c, d) in zip(ev, wall_ev):
+            flush.fill_(1)
+            c.record()
+            step.append()
+            a.record()
+            step.attention()
+            b.record()
+            d.record()
+        torch.cuda.synchronize()
+        wall = float(np.mean([c.elapsed_time(d) for c, d in wall_ev])) / 1e3
+    attn = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    return wall, float(np.mean(attn)), float(np.median(attn)), float(np.min(attn))
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_attention_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(st, budget_s: float = 15.0):
+    """The float64 oracle on the host cores over the first sequences of the
+    workload, batched 16 sequences per call, until about ``budget_s`` seconds
+    of oracle time.  Only the oracle calls are timed (page gather + math)."""
+    import oracle
+    q_dev = st.make_q("cuda")
+    spent, covered, seqs = 0.0, 0, 0
+    qsl = st.query_start_loc()
+    while seqs < st.num_seqs and spent < budget_s:
+        batch = list(range(seqs, min(seqs + 16, st.num_seqs)))
+        ks, vs, bts, lens, qs, qls = [], [], [], [], [], []
+        page0 = 0
+        for s in batch:
+            k, v = st.seq_kv(s, "cuda")
+            L = k.shape[0]
+            npg = (L + 15) // 16
+            pad = npg * 16 - L
+            shp = (pad, st.num_kv_heads, st.head_dim)
+            ks.append(torch.cat([k, torch.zeros(shp, dtype=k.dtype, device=k.device)]).cpu())
+            vs.append(torch.cat([v, torch.zeros(shp, dtype=v.dtype, device=v.device)]).cpu())
+            bts.append(np.arange(page0, page0 + npg, dtype=np.int32))
+            page0 += npg
+            lens.append(L)
+            qs.append(q_dev[qsl[s]:qsl[s + 1]].cpu())
+            qls.append(qsl[s + 1] - qsl[s])
+        kpool = torch.cat(ks).view(page0, 16, st.num_kv_heads, st.head_dim).transpose(1, 2).contiguous()
+        vpool = torch.cat(vs).view(page0, 16, st.num_kv_heads, st.head_dim).transpose(1, 2).contiguous()
+        width = max(len(b) for b in bts)
+        bt = np.zeros((len(batch), width), np.int32)
+        for i, b in enumerate(bts):
+            bt[i, :len(b)] = b
+        qcat = torch.cat(qs)
+        qsl_b = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.oracle_attention(qcat, kpool, vpool, bt, lens, qsl_b, st.scale)
+        spent += time.perf_counter() - t0
+        covered += sum(lens)
+        seqs += len(batch)
+        del kpool, vpool
+    e = 2 if st.dtype == torch.bfloat16 else 4
+    kvb = covered * 2 * st.num_kv_heads * st.head_dim * e
+    return {"value": kvb / spent / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "tokens_per_s": seqs / spent,
+            "sample": f"first {seqs} of {st.num_seqs} sequences ({covered} keys, "
+                      f"{kvb / 1e9:.2f} GB of K/V), {spent:.1f} s of oracle time"}
+
+
+def extra_prefill(steps: int, warmup: int):
+    """Mixed chunked-prefill workload (16 sequences: two 512-token chunks at
+    offsets 4608 and 4601 plus 14 decodes): packed-step tokens/s, and the
+    prefill kernel alone (the two chunks as their own step) against the dense
+    bf16 matrix peak."""
+    mixed = W.config_step(3, poison=False)
+    sm = Step(mixed, gen_device="cuda")
+    wall, attn, _, _ = time_steps(sm, steps, warmup, flush_bytes=1 << 30)
+    res = {"workload": mixed.name, "packed_step_tokens_per_s": mixed.total_q / wall,
+           "step_ms": wall * 1e3, "attention_ms": attn * 1e3}
+    del sm
+    torch.cuda.empty_cache()
+    idx = [i for i, n in enumerate(mixed.q_lens) if n > 1]
+    pre = W.build_step("mixed-prefill-chunks", [mixed.seq_lens[i] for i in idx],
+                       [mixed.q_lens[i] for i in idx], 32, 8, 128, torch.bfloat16, 3000,
+                       poison=False)
+    sp = Step(pre, gen_device="cuda")
+    _, pattn, pmed, _ = time_steps(sp, steps, warmup, flush_bytes=1 << 30)
+    fl = prefill_flops(pre)
+    res.update({"prefill_gflop": fl / 1e9, "prefill_ms": pattn * 1e3,
+                "prefill_tflops": fl / pattn / 1e12,
+                "prefill_mfma_util": fl / pattn / 1e12 / BF16_DENSE_TFLOPS})
+    del sp
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.manual_seed(0)
+    k = args.config
+    if k == 4:
+        run_main = bench_agent
+    else:
+        run_main = bench_single
+    rec = run_main(k, args)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_single(k, args):
+    st = W.config_step(k, poison=False)
+    log(f"workload {st.name}: {st.num_seqs} seqs, {sum(st.real_lens)} keys, "
+        f"{kv_bytes(st) / 1e9:.3f} GB K/V")
+    step = Step(st, gen_device="cuda")
+    flush = 0 if k == 5 else (1 << 30)   # the large batch outgrows every cache by itself
+    wall, attn_mean, attn_med, attn_min = time_steps(step, args.steps, args.warmup, flush)
+    kvb = kv_bytes(st)
+    gbs = kvb / wall / 1e9
+    achieved = kvb / attn_mean / 1e9
+    log(f"step {wall * 1e3:.3f} ms, attention mean {attn_mean * 1e3:.3f} ms "
+        f"(median {attn_med * 1e3:.3f}, min {attn_min * 1e3:.3f}) -> {achieved:.0f} GB/s")
+    rec = {
+        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if st.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic N(0,1) K/V/q, seeded; pool pages shuffled",
+        "config": {"workload": st.name, "num_seqs": st.num_seqs,
+                   "context_keys_total": int(sum(st.real_lens)), "max_seqlen_k": st.max_seqlen_k,
+                   "q_heads": st.num_q_heads, "kv_heads": st.num_kv_heads,
+                   "head_dim": st.head_dim, "page_size": st.block_size,
+                   "tokens_per_step": st.total_q, "kv_bytes_per_step": kvb,
+                   "cache_flush_between_steps": bool(flush)},
+        "hbm_peak_frac": gbs / HBM_PEAK_GBS,
+        "packed_step_tokens_per_s": st.total_q / wall,
+        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(f"decode_{st.name}"),
+                     "launch_ms_mean": attn_mean * 1e3, "launch_ms_median": attn_med * 1e3,
+                     "algorithmic_bytes_per_launch": kvb},
+    }
+    del step
+    torch.cuda.empty_cache()
+    if not args.no_extra and k != 3:
+        rec["extra"] = extra_prefill(min(args.steps, 20), args.warmup)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(st)
+    return rec
+
+
+def bench_agent(k, args):
+    run = W.AgentRun(poison=False)
+    b = run.base
+    kp, vp = b.new_pool("cuda", poison=False)
+    kf, vf, sf = run.prefill_rows("cuda")
+    pkv.pkv_append(kf, vf, kp, vp, sf)
+    del kf, vf, sf
+    msk = max(run.prompt) + run.steps
+    need = pkv.pkv_attention_workspace_size(b.num_seqs, b.num_seqs, 1, msk, b.num_q_heads,
+                                            b.num_kv_heads, b.head_dim, 16, b.dtype)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    qsl = torch.arange(b.num_seqs + 1, dtype=torch.int32, device="cuda")
+    steps = []
+    for i in range(run.steps):
+        pos, slots, bt, sl = run.step(i)
+        kn, vn = run.step_rows(i, "cuda")
+        steps.append((kn, vn, torch.from_numpy(slots).cuda(), torch.from_numpy(bt).cuda(),
+                      torch.tensor(sl, dtype=torch.int32, device="cuda"), run.step_q(i, "cuda"), sl))
+    out = torch.empty_like(steps[0][5])
+
+    def loop(ev=None):
+        for i, (kn, vn, sl_, bt, sls, q, _) in enumerate(steps):
+            pkv.pkv_append(kn, vn, kp, vp, sl_)
+            if ev is not None:
+                ev[i][0].record()
+            pkv.pkv_attention(q, kp, vp, bt, sls, qsl, b.scale, max_seqlen_q=1, max_seqlen_k=msk,
+                              out=out, workspace=ws)
+            if ev is not None:
+                ev[i][1].record()
+
+    loop()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in steps]
+    t0 = time.perf_counter()
+    loop(ev)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / len(steps)
+    attn = float(np.mean([a.elapsed_time(c) for a, c in ev])) / 1e3
+    logical = sum(sum(s[6]) for s in steps) * 2 * b.num_kv_heads * b.head_dim * 2 / len(steps)
+    unique = logical - (b.num_seqs - 1) * 512 * 2 * b.num_kv_heads * b.head_dim * 2
+    return {
+        "metric": METRIC, "value": unique / wall / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": len(steps), "warmup": 1, "ms_per_step": wall * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0,1), seeded; 512-token prefix in shared pages",
+        "config": {"workload": b.name, "num_seqs": b.num_seqs, "decode_steps": run.steps,
+                   "q_heads": b.num_q_heads, "kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                   "page_size": 16, "logical_kv_bytes_per_step": logical,
+                   "unique_kv_bytes_per_step": unique},
+        "packed_step_tokens_per_s": b.num_seqs / wall,
+        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
+                     "achieved": unique / attn / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": unique / attn / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "launch_ms_mean": attn * 1e3, "algorithmic_bytes_per_launch": unique},
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * pkv.h -- C ABI of the paged-KV attention library for one continuous-batching
+ * engine step on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  An engine step packs the query tokens of many sequences onto
+ * one token axis, with query_start_loc marking where each sequence's tokens
+ * begin; prefill chunks and single-token decodes share the step.  Keys and
+ * values live in fixed-size pages of a pool reserved once; each sequence's
+ * block-table row lists the physical pages of its logical pages.  (vllm-metal
+ * v0.4.0 release post: "How vllm-metal fits into vLLM", the runner receives a
+ * packed step plus block tables; "Replacing attention, reusing the rest",
+ * packed query axis with cu_seqlens, paged KV, one launch for prefill chunks
+ * and decode tokens; "Set a predictable memory budget", one pool reserved at
+ * startup serves every request.)
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless the argument says "host".
+ *   - All memory is owned by the caller.  The library allocates nothing and
+ *     keeps no state between calls except the thread-local error text.
+ *   - Calls only enqueue kernels on `stream` (a hipStream_t; NULL is the null
+ *     stream) and never synchronise, so they can be captured in a HIP graph.
+ *   - Return PKV_OK (0) or a negative PKV_E_* code; the reason is available
+ *     from pkv_last_error().  Host arguments are validated before anything is
+ *     launched; an invalid call launches nothing.
+ *   - Device-array contents are not validated on the hot path.  Values outside
+ *     the documented ranges give unspecified output, but the kernels clamp
+ *     every index they follow, so they never access memory outside the
+ *     buffers whose sizes the host arguments describe.  pkv_check_metadata()
+ *     and pkv_check_slots() validate host copies when a caller wants that.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, out        [total_q][num_q_heads][head_dim]        element type `dtype`
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim]    element type `dtype`
+ *   k_pool,v_pool [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32
+ *   seq_lens      [num_seqs] int32: keys of the sequence, this step's tokens included
+ *   query_start_loc [num_seqs + 1] int32, [0] = 0, [num_seqs] = total_q, non-decreasing
+ *   kv_start      [num_seqs] int32 or NULL: keys below kv_start[s] are masked
+ *   slot_mapping  [num_tokens] int64: block * block_size + offset, negative = skip
+ *
+ * Query token i of a sequence with n = query_start_loc[s+1] - query_start_loc[s]
+ * tokens and L = seq_lens[s] keys sits at position L - n + i and attends to
+ * keys kv_start[s] .. L - n + i (causal inside a chunk, aligned to its end).
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_F32 = 0,  /* float32 q, K/V and out */
+    PKV_BF16 = 1  /* bfloat16 q, K/V and out; float32 accumulation */
+} pkv_dtype_t;
+
+enum {
+    PKV_OK = 0,
+    PKV_E_ARG = -1,         /* a host argument is invalid (size, null pointer, ...) */
+    PKV_E_UNSUPPORTED = -2, /* valid but not built: head_dim, block_size, dtype, group size */
+    PKV_E_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    PKV_E_HIP = -4,         /* the HIP runtime reported an error at launch */
+    PKV_E_METADATA = -5     /* pkv_check_*: host metadata violates the contract */
+};
+
+/*
+ * pkv_append -- write this step's new key and value rows into their pool slots.
+ *
+ * For every token t with slot_mapping[t] >= 0, copies k_new[t][h][:] to
+ * k_pool[slot / block_size][h][slot % block_size][:] for every kv head h, and
+ * the same for v.  A pure byte copy: the pool is updated in place, never
+ * copied as a whole (vllm-metal v0.4.0 release post, "Prefix caching on hybrid
+ * models": rows are written in place instead of copying the pool; "Replacing
+ * attention, reusing the rest": admitted requests grow without reshaping).
+ *
+ * slot_mapping entries must be unique among non-negative values and lie in
+ * [0, num_blocks * block_size); a slot outside that range is skipped.  Pages
+ * shared by several sequences (a common prefix) must not be targeted.
+ * Supported: dtype F32/BF16, head_dim 64 or 128, any block_size in [1, 256].
+ * num_tokens == 0 returns PKV_OK without launching.
+ */
+int pkv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+               const int64_t *slot_mapping, int64_t num_tokens, int num_kv_heads,
+               int head_dim, int block_size, int64_t num_blocks, pkv_dtype_t dtype,
+               void *stream);
+
+/*
+ * pkv_attention_workspace_size -- bytes of device workspace pkv_attention needs
+ * for a step with these host bounds (host-only, pure; 0 if none is needed).
+ * The same arguments must be passed to pkv_attention.  The workspace holds the
+ * float32 partial results of the split-key decode pass.
+ */
+size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqlen_q,
+                                    int max_seqlen_k, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, pkv_dtype_t dtype);
+
+/*
+ * pkv_attention -- attention for one packed step through the block tables.
+ *
+ * out[t][h][:] = sum_j softmax_j(scale * q[t][h] . K_j) * V_j over the keys
+ * the token sees (see the header comment), K_j and V_j read from kv head
+ * h / (num_q_heads / num_kv_heads) of the page block_tables[s][j / block_size]
+ * at offset j % block_size.  Pages may be shared by several sequences (a common
+ * prefix); they are only read.  Bytes of the pool outside the visible keys,
+ * including the rest of a sequence's last page and pages below kv_start, are
+ * never allowed to reach the output, whatever they hold (NaN included).
+ * (vllm-metal v0.4.0 release post, "Replacing attention, reusing the rest";
+ * left padding with masked leading keys: vllm-ios README, "How it works" and
+ * "What this is and isn't".)
+ *
+ * Host bounds: max_seqlen_q >= every sequence's query count, max_seqlen_k >=
+ * every seq_lens[s]; both size the launch grids.  total_q = query_start_loc
+ * [num_seqs].  Sequences with one query token take the split-key decode path;
+ * sequences with two or more take the chunked-prefill path.  A sequence with
+ * zero query tokens contributes nothing.
+ *
+ * Supported: dtype F32/BF16 (q, pools and out share it), head_dim 64 or 128,
+ * block_size 16, num_q_heads % num_kv_heads == 0 and 1 <= group size <= 16.
+ * out must not alias q or the pools.  workspace must hold at least
+ * pkv_attention_workspace_size(...) bytes (it may be NULL when that is 0).
+ * num_seqs == 0 or total_q == 0 returns PKV_OK without launching.
+ */
+int pkv_attention(void *out, const void *q, const void *k_pool, const void *v_pool,
+                  const int32_t *block_tables, const int32_t *seq_lens,
+                  const int32_t *query_start_loc, const int32_t *kv_start, int num_seqs,
+                  int64_t total_q, int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int64_t num_blocks, float scale, pkv_dtype_t dtype, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
+ * pkv_check_metadata -- validate HOST copies of the step metadata against the
+ * contract above: query_start_loc starts at 0, is non-decreasing and ends at
+ * total_q; 0 <= kv_start[s] <= seq_lens[s]; each sequence's query count is at
+ * most seq_lens[s] - kv_start[s]; every page a visible key lives on is listed
+ * and lies in [0, num_blocks).  Returns PKV_OK or PKV_E_METADATA (reason in
+ * pkv_last_error()).  kv_start may be NULL.
+ */
+int pkv_check_metadata(const int32_t *block_tables, const int32_t *seq_lens,
+                       const int32_t *query_start_loc, const int32_t *kv_start, int num_seqs,
+                       int64_t total_q, int max_blocks_per_seq, int block_size,
+                       int64_t num_blocks);
+
+/*
+ * pkv_check_slots -- validate a HOST copy of a slot mapping: every
+ * non-negative slot lies in [0, num_blocks * block_size) and appears once.
+ * Returns PKV_OK or PKV_E_METADATA.
+ */
+int pkv_check_slots(const int64_t *slot_mapping, int64_t num_tokens, int block_size,
+                    int64_t num_blocks);
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the
+ * next pkv_* call on the same thread. */
+const char *pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -173,10 +173,12 @@ int oracle_attention(double *out, const void *q, const void *k_pool, const void 
         double *Kc = (double *)malloc((size_t)(nk > 0 ? nk : 1) * D * sizeof(double));
         double *Vc = (double *)malloc((size_t)(nk > 0 ? nk : 1) * D * sizeof(double));
         double *w = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
-        if (!Kc || !Vc || !w) {
+        double *qd = (double *)malloc((size_t)D * sizeof(double));
+        if (!Kc || !Vc || !w || !qd) {
             free(Kc);
             free(Vc);
             free(w);
+            free(qd);
             failed |= 1;
             continue;
         }
@@ -202,11 +204,13 @@ int oracle_attention(double *out, const void *q, const void *k_pool, const void 
                 if (last < a)
                     continue;
                 const int64_t qb = (t * num_q_heads + h) * (int64_t)D;
+                for (int d = 0; d < D; ++d)
+                    qd[d] = orc_elem(q, qb + d, dtype);
                 double m = -INFINITY;
                 for (int64_t j = a; j <= last; ++j) {
                     double acc = 0.0;
                     for (int d = 0; d < D; ++d)
-                        acc += orc_elem(q, qb + d, dtype) * Kc[(j - a) * D + d];
+                        acc += qd[d] * Kc[(j - a) * D + d];
                     w[j - a] = scale * acc;
                     if (w[j - a] > m)
                         m = w[j - a];
@@ -228,6 +232,7 @@ int oracle_attention(double *out, const void *q, const void *k_pool, const void 
         free(Kc);
         free(Vc);
         free(w);
+        free(qd);
     }
     return failed ? ORC_E_NOMEM : ORC_OK;
 }

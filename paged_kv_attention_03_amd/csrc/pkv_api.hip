@@ -1,0 +1,391 @@
+// C ABI of the paged-KV attention library (declared in include/pkv.h).
+//
+// Host side: argument validation (before any launch), the launch planner
+// (which sequences take the decode or the prefill path, the split size of the
+// decode pass, workspace layout), kernel launches on the caller's stream, and
+// host-copy metadata checkers.  The library allocates nothing and never
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pkv.h"
+#include "append.hpp"
+#include "decode.hpp"
+#include "prefill.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return PKV_OK;
+}
+
+int hip_status(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return PKV_OK;
+}
+
+size_t elem_bytes(pkv_dtype_t dt) { return dt == PKV_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+// ---------------------------------------------------------------- planner
+
+struct Plan {
+    int pages_per_split = 1;
+    int max_splits = 1;
+    int prefill_tile_tokens = 0;
+    size_t ws_o_bytes = 0;
+    size_t ws_ml_bytes = 0;
+    size_t ws_bytes() const { return ws_o_bytes + ws_ml_bytes; }
+};
+
+constexpr int kBlock = 16;
+// Decode workgroups the planner aims for: enough single-wavefront workgroups
+// to keep every CU of an MI355X (256 CUs, several waves each) streaming pages.
+constexpr long kDecodeTargetWG = 16384;
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+Plan make_plan(int num_seqs, int max_seqlen_k, int num_q_heads, int num_kv_heads,
+               int head_dim, int group) {
+    Plan pl;
+    const long max_pages = (max_seqlen_k + kBlock - 1) / kBlock;
+    // Units of (sequence, kv head) times pages, spread over the target number of
+    // workgroups; an even split keeps whole page pairs per workgroup.
+    long est = (long)num_seqs * num_kv_heads * max_pages;
+    long pps = (est + kDecodeTargetWG - 1) / kDecodeTargetWG;
+    if (pps < 8) pps = 8;
+    if (pps > 512) pps = 512;
+    pps = (pps + 1) & ~1L;
+    const int forced = env_int("PKV_DECODE_PAGES_PER_SPLIT", 0);
+    if (forced > 0) pps = (forced + 1) & ~1;
+    pl.pages_per_split = (int)pps;
+    pl.max_splits = (int)((max_pages + pps - 1) / pps);
+    if (pl.max_splits < 1) pl.max_splits = 1;
+    pl.prefill_tile_tokens = pkv::kPrefillRows / group;
+    if (pl.max_splits > 1) {
+        const size_t slots = (size_t)num_seqs * num_q_heads * pl.max_splits;
+        pl.ws_o_bytes = slots * head_dim * sizeof(float);
+        pl.ws_ml_bytes = slots * 2 * sizeof(float);
+    }
+    return pl;
+}
+
+int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 pkv_dtype_t dtype) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16)
+        return fail(PKV_E_UNSUPPORTED, "dtype %d is not supported (PKV_F32 or PKV_BF16)", (int)dtype);
+    if (num_q_heads <= 0 || num_kv_heads <= 0)
+        return fail(PKV_E_ARG, "head counts must be positive (q %d, kv %d)", num_q_heads, num_kv_heads);
+    if (num_q_heads % num_kv_heads != 0)
+        return fail(PKV_E_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                    num_kv_heads);
+    if (num_q_heads / num_kv_heads > 16)
+        return fail(PKV_E_UNSUPPORTED, "group size %d > 16 is not supported",
+                    num_q_heads / num_kv_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_E_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+    if (block_size != kBlock)
+        return fail(PKV_E_UNSUPPORTED, "block_size %d is not supported (16)", block_size);
+    return PKV_OK;
+}
+
+template <typename T, int D>
+int launch_attention(const pkv::DecodeParams& dp, const pkv::MergeParams& mp,
+                     const pkv::PrefillParams& pp, int max_seqlen_q, int64_t total_q, int num_seqs,
+                     hipStream_t stream) {
+    const long dgrid = (long)dp.max_splits * dp.Hkv * num_seqs;
+    hipLaunchKernelGGL((pkv::decode_kernel<T, D>), dim3((unsigned)dgrid), dim3(64), 0, stream, dp);
+    if (int rc = hip_status("decode launch")) return rc;
+    if (dp.max_splits > 1) {
+        hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)),
+                           dim3(64), 0, stream, mp);
+        if (int rc = hip_status("merge launch")) return rc;
+    }
+    if (max_seqlen_q > 1) {
+        const long tiles = (total_q + pp.tile_tokens - 1) / pp.tile_tokens + num_seqs;
+        hipLaunchKernelGGL((pkv::prefill_kernel<T, D>), dim3((unsigned)tiles, pp.Hkv),
+                           dim3(pkv::kPrefillWaves * 64), 0, stream, pp);
+        if (int rc = hip_status("prefill launch")) return rc;
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+int pkv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+               const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads, int head_dim,
+               int block_size, int64_t num_blocks, pkv_dtype_t dtype, void* stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16)
+        return fail(PKV_E_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    if (num_tokens < 0) return fail(PKV_E_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+    if (num_kv_heads <= 0) return fail(PKV_E_ARG, "num_kv_heads %d <= 0", num_kv_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_E_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+    if (block_size < 1 || block_size > 256)
+        return fail(PKV_E_UNSUPPORTED, "block_size %d outside [1, 256]", block_size);
+    if (num_blocks <= 0) return fail(PKV_E_ARG, "num_blocks %lld <= 0", (long long)num_blocks);
+    if (num_tokens == 0) return ok();
+    if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
+        return fail(PKV_E_ARG, "null pointer argument");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKV_E_ARG, "K/V buffers must be 16-byte aligned");
+    const size_t rb = (size_t)head_dim * elem_bytes(dtype);
+    const size_t pool_bytes = (size_t)num_blocks * num_kv_heads * block_size * rb;
+    const size_t new_bytes = (size_t)num_tokens * num_kv_heads * rb;
+    if (overlaps(k_new, new_bytes, k_pool, pool_bytes) || overlaps(v_new, new_bytes, v_pool, pool_bytes) ||
+        overlaps(k_pool, pool_bytes, v_pool, pool_bytes))
+        return fail(PKV_E_ARG, "new rows and pools must not overlap");
+    pkv::AppendParams ap;
+    ap.k_new = static_cast<const uint8_t*>(k_new);
+    ap.v_new = static_cast<const uint8_t*>(v_new);
+    ap.k_pool = static_cast<uint8_t*>(k_pool);
+    ap.v_pool = static_cast<uint8_t*>(v_pool);
+    ap.slots = slot_mapping;
+    ap.rows = num_tokens * num_kv_heads;
+    ap.num_kv_heads = num_kv_heads;
+    ap.chunks_per_row = (int)(rb / 16);
+    ap.block_size = block_size;
+    ap.num_slots = num_blocks * block_size;
+    const int64_t threads = ap.rows * ap.chunks_per_row;
+    const int64_t grid = (threads + 255) / 256;
+    if (grid > 0x7fffffffLL) return fail(PKV_E_ARG, "too many tokens for one launch");
+    hipLaunchKernelGGL(pkv::append_kernel, dim3((unsigned)grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), ap);
+    if (int rc = hip_status("append launch")) return rc;
+    return ok();
+}
+
+size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqlen_q,
+                                    int max_seqlen_k, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, pkv_dtype_t dtype) {
+    (void)total_q;
+    (void)max_seqlen_q;
+    (void)dtype;
+    if (num_seqs <= 0 || max_seqlen_k <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || block_size != kBlock || num_q_heads % num_kv_heads)
+        return 0;
+    return make_plan(num_seqs, max_seqlen_k, num_q_heads, num_kv_heads, head_dim,
+                     num_q_heads / num_kv_heads)
+        .ws_bytes();
+}
+
+int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, const int32_t* seq_lens,
+                  const int32_t* query_start_loc, const int32_t* kv_start, int num_seqs,
+                  int64_t total_q, int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int64_t num_blocks, float scale, pkv_dtype_t dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    if (int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype)) return rc;
+    if (num_seqs < 0) return fail(PKV_E_ARG, "num_seqs %d < 0", num_seqs);
+    if (total_q < 0) return fail(PKV_E_ARG, "total_q %lld < 0", (long long)total_q);
+    if (num_seqs == 0 || total_q == 0) return ok();
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc)
+        return fail(PKV_E_ARG, "null pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKV_E_ARG, "q, out and the pools must be 16-byte aligned");
+    if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "max_blocks_per_seq %d <= 0", max_blocks_per_seq);
+    if (num_blocks <= 0) return fail(PKV_E_ARG, "num_blocks %lld <= 0", (long long)num_blocks);
+    if (max_seqlen_q <= 0 || max_seqlen_k <= 0)
+        return fail(PKV_E_ARG, "max_seqlen_q %d and max_seqlen_k %d must be positive", max_seqlen_q,
+                    max_seqlen_k);
+    if (max_seqlen_q > max_seqlen_k)
+        return fail(PKV_E_ARG, "max_seqlen_q %d > max_seqlen_k %d", max_seqlen_q, max_seqlen_k);
+    if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PKV_E_ARG, "max_seqlen_k %d exceeds the block-table width (%d pages of %d)",
+                    max_seqlen_k, max_blocks_per_seq, block_size);
+    if (total_q > 0x7fffffffLL) return fail(PKV_E_ARG, "total_q too large");
+    if (!std::isfinite(scale)) return fail(PKV_E_ARG, "scale is not finite");
+    const size_t eb = elem_bytes(dtype);
+    const size_t io_bytes = (size_t)total_q * num_q_heads * head_dim * eb;
+    const size_t pool_bytes = (size_t)num_blocks * num_kv_heads * block_size * head_dim * eb;
+    if (overlaps(out, io_bytes, q, io_bytes) || overlaps(out, io_bytes, k_pool, pool_bytes) ||
+        overlaps(out, io_bytes, v_pool, pool_bytes))
+        return fail(PKV_E_ARG, "out must not alias q or the pools");
+
+    const int G = num_q_heads / num_kv_heads;
+    const Plan pl = make_plan(num_seqs, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, G);
+    if (pl.ws_bytes() > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes())
+            return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                        workspace ? workspace_bytes : (size_t)0, pl.ws_bytes());
+        if (!aligned16(workspace)) return fail(PKV_E_ARG, "workspace must be 16-byte aligned");
+        if (overlaps(workspace, pl.ws_bytes(), out, io_bytes))
+            return fail(PKV_E_ARG, "workspace must not alias out");
+    }
+    const float scale_log2 = scale * 1.4426950408889634f;
+    float* ws_o = pl.ws_bytes() ? static_cast<float*>(workspace) : nullptr;
+    float* ws_ml = pl.ws_bytes() ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes)
+                                 : nullptr;
+
+    pkv::DecodeParams dp;
+    dp.out = out;
+    dp.q = q;
+    dp.k_pool = k_pool;
+    dp.v_pool = v_pool;
+    dp.block_tables = block_tables;
+    dp.seq_lens = seq_lens;
+    dp.qsl = query_start_loc;
+    dp.kv_start = kv_start;
+    dp.ws_o = ws_o;
+    dp.ws_ml = ws_ml;
+    dp.num_seqs = num_seqs;
+    dp.max_blocks = max_blocks_per_seq;
+    dp.Hq = num_q_heads;
+    dp.Hkv = num_kv_heads;
+    dp.G = G;
+    dp.pages_per_split = pl.pages_per_split;
+    dp.max_splits = pl.max_splits;
+    dp.max_seqlen_k = max_seqlen_k;
+    dp.total_q = total_q;
+    dp.num_blocks = num_blocks;
+    dp.scale_log2 = scale_log2;
+
+    pkv::MergeParams mp;
+    mp.out = out;
+    mp.ws_o = ws_o;
+    mp.ws_ml = ws_ml;
+    mp.seq_lens = seq_lens;
+    mp.qsl = query_start_loc;
+    mp.kv_start = kv_start;
+    mp.num_seqs = num_seqs;
+    mp.max_blocks = max_blocks_per_seq;
+    mp.Hq = num_q_heads;
+    mp.pages_per_split = pl.pages_per_split;
+    mp.max_splits = pl.max_splits;
+    mp.max_seqlen_k = max_seqlen_k;
+    mp.total_q = total_q;
+
+    pkv::PrefillParams pp;
+    pp.out = out;
+    pp.q = q;
+    pp.k_pool = k_pool;
+    pp.v_pool = v_pool;
+    pp.block_tables = block_tables;
+    pp.seq_lens = seq_lens;
+    pp.qsl = query_start_loc;
+    pp.kv_start = kv_start;
+    pp.num_seqs = num_seqs;
+    pp.max_blocks = max_blocks_per_seq;
+    pp.Hq = num_q_heads;
+    pp.Hkv = num_kv_heads;
+    pp.G = G;
+    pp.tile_tokens = pl.prefill_tile_tokens;
+    pp.max_seqlen_k = max_seqlen_k;
+    pp.total_q = total_q;
+    pp.num_blocks = num_blocks;
+    pp.scale_log2 = scale_log2;
+
+    const long dgrid = (long)pl.max_splits * num_kv_heads * num_seqs;
+    if (dgrid > 0x7fffffffL) return fail(PKV_E_ARG, "decode grid too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc;
+    if (dtype == PKV_BF16)
+        rc = head_dim == 128 ? launch_attention<pkv::bf16_t, 128>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
+                             : launch_attention<pkv::bf16_t, 64>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
+    else
+        rc = head_dim == 128 ? launch_attention<float, 128>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
+                             : launch_attention<float, 64>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
+    if (rc) return rc;
+    return ok();
+}
+
+int pkv_check_metadata(const int32_t* block_tables, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, const int32_t* kv_start, int num_seqs,
+                       int64_t total_q, int max_blocks_per_seq, int block_size, int64_t num_blocks) {
+    if (num_seqs < 0 || block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+        return fail(PKV_E_ARG, "invalid sizes");
+    if (num_seqs == 0) return ok();
+    if (!block_tables || !seq_lens || !query_start_loc)
+        return fail(PKV_E_ARG, "null pointer argument");
+    if (query_start_loc[0] != 0) return fail(PKV_E_METADATA, "query_start_loc[0] = %d, not 0", query_start_loc[0]);
+    if (query_start_loc[num_seqs] != total_q)
+        return fail(PKV_E_METADATA, "query_start_loc[%d] = %d, not total_q %lld", num_seqs,
+                    query_start_loc[num_seqs], (long long)total_q);
+    for (int s = 0; s < num_seqs; ++s) {
+        const int64_t n = (int64_t)query_start_loc[s + 1] - query_start_loc[s];
+        const int64_t L = seq_lens[s];
+        const int64_t a = kv_start ? kv_start[s] : 0;
+        if (n < 0) return fail(PKV_E_METADATA, "query_start_loc decreases at sequence %d", s);
+        if (L < 0) return fail(PKV_E_METADATA, "seq_lens[%d] = %lld < 0", s, (long long)L);
+        if (a < 0 || a > L)
+            return fail(PKV_E_METADATA, "kv_start[%d] = %lld outside [0, %lld]", s, (long long)a, (long long)L);
+        if (n > L - a)
+            return fail(PKV_E_METADATA, "sequence %d has %lld query tokens but %lld visible keys", s,
+                        (long long)n, (long long)(L - a));
+        if (L == 0) continue;
+        const int64_t last = (L - 1) / block_size;
+        if (last >= max_blocks_per_seq)
+            return fail(PKV_E_METADATA, "sequence %d needs %lld pages, block table has %d", s,
+                        (long long)(last + 1), max_blocks_per_seq);
+        for (int64_t pg = a / block_size; pg <= last; ++pg) {
+            const int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + pg];
+            if (b < 0 || b >= num_blocks)
+                return fail(PKV_E_METADATA, "block_tables[%d][%lld] = %d outside [0, %lld)", s,
+                            (long long)pg, b, (long long)num_blocks);
+        }
+    }
+    return ok();
+}
+
+int pkv_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int block_size,
+                    int64_t num_blocks) {
+    if (num_tokens < 0 || block_size <= 0 || num_blocks < 0) return fail(PKV_E_ARG, "invalid sizes");
+    if (num_tokens == 0) return ok();
+    if (!slot_mapping) return fail(PKV_E_ARG, "null pointer argument");
+    const int64_t nslots = num_blocks * block_size;
+    std::vector<int64_t> seen;
+    seen.reserve((size_t)num_tokens);
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const int64_t v = slot_mapping[t];
+        if (v < 0) continue;
+        if (v >= nslots)
+            return fail(PKV_E_METADATA, "slot_mapping[%lld] = %lld outside [0, %lld)", (long long)t,
+                        (long long)v, (long long)nslots);
+        seen.push_back(v);
+    }
+    std::sort(seen.begin(), seen.end());
+    for (size_t i = 1; i < seen.size(); ++i)
+        if (seen[i] == seen[i - 1])
+            return fail(PKV_E_METADATA, "slot %lld is written twice", (long long)seen[i]);
+    return ok();
+}
+
+}  // extern "C"

@@ -141,11 +141,15 @@ class StepInputs:
         return (torch.full(shape, fill, dtype=self.dtype, device=dev),
                 torch.full(shape, fill, dtype=self.dtype, device=dev))
 
-    def rows(self, which: str, device=None, seqs: Optional[Sequence[int]] = None):
+    def rows(self, which: str, device=None, seqs: Optional[Sequence[int]] = None,
+             gen_device=None):
         """Concatenated (k, v, slot_mapping) of the rows written before the step
         (``which='fill'``) or by the step itself (``which='step'``).  Shared
-        prefix rows are written once, by the first sequence that holds them."""
+        prefix rows are written once, by the first sequence that holds them.
+        Rows are drawn on ``gen_device`` (default: ``device``) and placed on
+        ``device``."""
         dev = device or self.device
+        gdev = gen_device or dev
         ks, vs, sl = [], [], []
         written_prefix = False
         for s in (range(self.num_seqs) if seqs is None else seqs):
@@ -154,7 +158,7 @@ class StepInputs:
             lo, hi = (0, n - qn) if which == "fill" else (n - qn, n)
             if hi <= lo:
                 continue
-            k, v = self.seq_kv(s, dev)
+            k, v = self.seq_kv(s, gdev)
             idx = np.arange(lo, hi)
             if self.shared_prefix > 0:
                 if written_prefix:
@@ -163,9 +167,9 @@ class StepInputs:
                     written_prefix = True
             if idx.size == 0:
                 continue
-            sel = torch.from_numpy(idx).to(dev)
-            ks.append(k.index_select(0, sel))
-            vs.append(v.index_select(0, sel))
+            sel = torch.from_numpy(idx).to(gdev)
+            ks.append(k.index_select(0, sel).to(dev))
+            vs.append(v.index_select(0, sel).to(dev))
             sl.append(self.token_slots[s][idx])
         shp = (0, self.num_kv_heads, self.head_dim)
         if not ks:
@@ -174,10 +178,10 @@ class StepInputs:
         slots = torch.from_numpy(np.concatenate(sl).astype(np.int64)).to(dev)
         return torch.cat(ks, 0), torch.cat(vs, 0), slots
 
-    def make_q(self, device=None):
+    def make_q(self, device=None, gen_device=None):
         dev = device or self.device
-        return randn((self.total_q, self.num_q_heads, self.head_dim), self.seed + 1, dev,
-                     self.dtype)
+        return randn((self.total_q, self.num_q_heads, self.head_dim), self.seed + 1,
+                     gen_device or dev, self.dtype).to(dev)
 
 
 def _assign_pages(real_lens, kv_pad, block_size, free, shared_prefix, max_blocks):
@@ -405,9 +409,8 @@ class AgentRun:
         bs = b.block_size
         pos = [p + i for p in self.prompt]        # position of the new token
         for s in range(b.num_seqs):
-            pg = pos[s] // bs
-            if pos[s] % bs == 0:                  # crossing into a fresh page
-                self.block_tables[s, pg] = self._bt_full[s, pg]
+            npg = pos[s] // bs + 1                # a page crossing adds one entry
+            self.block_tables[s, :npg] = self._bt_full[s, :npg]
         slots = np.array([b.token_slots[s][pos[s]] for s in range(b.num_seqs)], dtype=np.int64)
         seq_lens = [p + 1 for p in pos]
         return pos, slots, self.block_tables.copy(), seq_lens

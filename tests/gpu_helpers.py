@@ -1,0 +1,89 @@
+"""Helpers for the GPU parity tests: run a generated step through the C ABI
+(via the Python binding) and compare with the float64 oracle.  Test code."""
+import math
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_attention_03_amd as pkv
+from tests.helpers import close
+
+# elementwise |gpu - oracle| <= atol + rtol * |oracle|
+TOL = {torch.bfloat16: (1e-2, 1e-2), torch.float32: (1e-5, 1e-5)}
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def gpu_pools(st, gen_device="cpu", poison=None):
+    """Device pools filled through pkv_append: the rows before the step, then
+    the step's own rows."""
+    kp, vp = st.new_pool("cuda", poison)
+    for which in ("fill", "step"):
+        k, v, sl = st.rows(which, "cuda", gen_device=gen_device)
+        if k.shape[0]:
+            pkv.pkv_append(k, v, kp, vp, sl)
+        del k, v, sl
+    return kp, vp
+
+
+def gpu_attention(st, q, kp, vp, **kw):
+    md = st.metadata("cuda")
+    out = pkv.pkv_attention(q, kp, vp, md["block_tables"], md["seq_lens"],
+                            md["query_start_loc"], st.scale, max_seqlen_q=st.max_seqlen_q,
+                            max_seqlen_k=st.max_seqlen_k, kv_start=md["kv_start"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_seq_outputs(st, q_host, seqs, gen_device="cpu", tokens=None):
+    """Oracle outputs of the listed sequences, from their real rows (drawn on
+    ``gen_device`` and copied to the host) laid out in a contiguous pool with an
+    identity block table, i.e. the ragged form of the sequence.  ``tokens``
+    optionally restricts sequence s to some of its query tokens (each computed
+    as the decode it is equivalent to).  Returns {s: float64 [n, Hq, D]}."""
+    qsl = st.query_start_loc()
+    res = {}
+    for s in seqs:
+        k, v = st.seq_kv(s, gen_device)
+        k, v = k.cpu(), v.cpu()
+        L = k.shape[0]
+        bs = 16
+        nb = max(1, (L + bs - 1) // bs)
+        kp = torch.full((nb, st.num_kv_heads, bs, st.head_dim), float("nan"), dtype=st.dtype)
+        vp = kp.clone()
+        kp, vp = oracle.oracle_append(kp, vp, k, v, np.arange(L, dtype=np.int64))
+        bt = np.arange(nb, dtype=np.int32)[None]
+        qrows = q_host[qsl[s]:qsl[s + 1]]
+        n = qrows.shape[0]
+        if tokens is None or s not in tokens:
+            res[s] = oracle.oracle_attention(qrows, kp, vp, bt, [L], [0, n], st.scale)
+        else:
+            outs = []
+            for i in tokens[s]:
+                outs.append(oracle.oracle_attention(qrows[i:i + 1], kp, vp, bt, [L - n + i + 1],
+                                                    [0, 1], st.scale))
+            res[s] = np.concatenate(outs)
+    return res
+
+
+def to_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_close(got, ref, dtype, what):
+    atol, rtol = TOL[dtype]
+    g = to_f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    ok, maxerr = close(g, ref, atol, rtol)
+    denom = float(np.linalg.norm(ref)) or 1.0
+    rel = float(np.linalg.norm(np.nan_to_num(g - ref, nan=1e30))) / denom
+    log(f"  {what}: max|err| {maxerr:.3e}  rel-L2 {rel:.3e}  finite {bool(np.isfinite(g).all())}")
+    assert ok, f"{what}: outside atol={atol} rtol={rtol} (max err {maxerr:.3e})"
+    return maxerr, rel
+
+
+def raw_bits(t: torch.Tensor) -> np.ndarray:
+    iv = torch.int16 if t.dtype == torch.bfloat16 else torch.int32
+    return t.detach().cpu().contiguous().view(iv).numpy()

@@ -1,0 +1,174 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects every invalid host argument before launching
+anything (so these run without a GPU; the pointers below are never
+dereferenced).  Also the host-copy metadata and slot checkers."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_03_amd as pkv
+from paged_kv_attention_03_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pkv.load_library()
+
+
+def test_header_entry_points_are_exported(lib):
+    hdr = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", hdr)))
+    assert {"pkv_append", "pkv_attention", "pkv_attention_workspace_size", "pkv_check_metadata",
+            "pkv_check_slots", "pkv_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pkv.h but not exported"
+
+
+def _attn(lib, **over):
+    a = dict(out=FAKE, q=FAKE + 0x10000000, k=FAKE + 0x20000000, v=FAKE + 0x30000000, bt=FAKE,
+             sl=FAKE, qsl=FAKE, ks=None, num_seqs=4, total_q=4, max_blocks=8, msq=1, msk=100,
+             hq=8, hkv=2, d=128, bs=16, nb=64, scale=0.125, dtype=pkv.PKV_BF16, ws=None,
+             ws_bytes=0, stream=None)
+    a.update(over)
+    return lib.pkv_attention(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["qsl"], a["ks"],
+                             a["num_seqs"], a["total_q"], a["max_blocks"], a["msq"], a["msk"],
+                             a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+                             a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=7), pkv.PKV_E_UNSUPPORTED),
+    (dict(hq=6, hkv=4), pkv.PKV_E_ARG),
+    (dict(hq=0), pkv.PKV_E_ARG),
+    (dict(hq=34, hkv=2), pkv.PKV_E_UNSUPPORTED),
+    (dict(d=96), pkv.PKV_E_UNSUPPORTED),
+    (dict(bs=32), pkv.PKV_E_UNSUPPORTED),
+    (dict(q=None), pkv.PKV_E_ARG),
+    (dict(bt=None), pkv.PKV_E_ARG),
+    (dict(q=FAKE + 0x10000008), pkv.PKV_E_ARG),
+    (dict(q=FAKE), pkv.PKV_E_ARG),                  # out aliases q
+    (dict(max_blocks=0), pkv.PKV_E_ARG),
+    (dict(msk=8 * 16 + 1), pkv.PKV_E_ARG),           # wider than the block table
+    (dict(msq=200), pkv.PKV_E_ARG),                  # more queries than keys
+    (dict(msq=0), pkv.PKV_E_ARG),
+    (dict(nb=0), pkv.PKV_E_ARG),
+    (dict(num_seqs=-1), pkv.PKV_E_ARG),
+    (dict(scale=float("nan")), pkv.PKV_E_ARG),
+])
+def test_attention_rejects_invalid_arguments(lib, over, code):
+    assert _attn(lib, **over) == code
+    assert pkv.pkv_last_error() != ""
+
+
+def test_attention_workspace_is_checked(lib):
+    need = lib.pkv_attention_workspace_size(128, 128, 1, 32768, 64, 8, 128, 16, pkv.PKV_BF16)
+    assert need > 0
+    common = dict(num_seqs=128, total_q=128, max_blocks=2048, msk=32768, hq=64, hkv=8)
+    assert _attn(lib, **common) == pkv.PKV_E_WORKSPACE
+    assert _attn(lib, ws=FAKE + 0x40000000, ws_bytes=need - 1, **common) == pkv.PKV_E_WORKSPACE
+    assert "workspace" in pkv.pkv_last_error()
+
+
+def test_empty_steps_launch_nothing(lib):
+    assert _attn(lib, num_seqs=0) == pkv.PKV_OK
+    assert _attn(lib, total_q=0) == pkv.PKV_OK
+    assert lib.pkv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 128, 16, 64, pkv.PKV_BF16, None) == 0
+
+
+def test_workspace_size_follows_the_plan(lib):
+    ws = lambda ns, msk, hq=16, hkv=8, d=128: lib.pkv_attention_workspace_size(
+        ns, ns, 1, msk, hq, hkv, d, 16, pkv.PKV_BF16)
+    assert ws(4, 100, 4, 2, 64) == 0           # a short context needs one split
+    big = ws(128, 32768, 64, 8)
+    assert big > 0 and big % 16 == 0
+    assert ws(0, 100) == 0
+    assert lib.pkv_attention_workspace_size(4, 4, 1, 100, 4, 2, 64, 32, pkv.PKV_BF16) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(d=96), pkv.PKV_E_UNSUPPORTED),
+    (dict(dtype=3), pkv.PKV_E_UNSUPPORTED),
+    (dict(bs=0), pkv.PKV_E_UNSUPPORTED),
+    (dict(hkv=0), pkv.PKV_E_ARG),
+    (dict(nb=0), pkv.PKV_E_ARG),
+    (dict(t=-1), pkv.PKV_E_ARG),
+    (dict(slots=None), pkv.PKV_E_ARG),
+    (dict(kn=FAKE + 4), pkv.PKV_E_ARG),
+    (dict(kn=FAKE + 0x200000), pkv.PKV_E_ARG),      # new rows inside the pool
+])
+def test_append_rejects_invalid_arguments(lib, args, code):
+    a = dict(kn=FAKE, vn=FAKE + 0x100000, kp=FAKE + 0x200000, vp=FAKE + 0x8000000, slots=FAKE,
+             t=4, hkv=2, d=128, bs=16, nb=64, dtype=pkv.PKV_BF16)
+    a.update(args)
+    rc = lib.pkv_append(a["kn"], a["vn"], a["kp"], a["vp"], a["slots"], a["t"], a["hkv"], a["d"],
+                        a["bs"], a["nb"], a["dtype"], None)
+    assert rc == code
+
+
+# ------------------------------------------------------------- host checkers
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_checker_accepts_every_config(k):
+    for padded in (False, True):
+        st = W.config_step(k, padded=padded)
+        md = st.metadata("cpu")
+        pkv.pkv_check_metadata(md["block_tables"], md["seq_lens"], md["query_start_loc"],
+                               md["kv_start"], st.total_q, st.block_size, st.num_blocks)
+        for which in ("fill", "step"):
+            slots = np.concatenate([st.token_slots[s] for s in range(st.num_seqs)])
+            pkv.pkv_check_slots(slots, st.block_size, st.num_blocks)
+
+
+def test_checker_accepts_agent_run_steps():
+    run = W.AgentRun(steps=70)
+    for i in (0, 35, 69):
+        pos, slots, bt, sl = run.step(i)
+        pkv.pkv_check_metadata(bt, sl, np.arange(17), None, 16, 16, run.base.num_blocks)
+        pkv.pkv_check_slots(slots, 16, run.base.num_blocks)
+
+
+def _meta():
+    st = W.config_step(1)
+    md = {k: (None if v is None else v.numpy().copy()) for k, v in st.metadata("cpu").items()}
+    return st, md
+
+
+@pytest.mark.parametrize("mutate", [
+    lambda m: m["query_start_loc"].__setitem__(0, 1),
+    lambda m: m["query_start_loc"].__setitem__(2, 0),           # decreasing
+    lambda m: m["block_tables"].__setitem__((0, 0), 64),         # outside the pool
+    lambda m: m["block_tables"].__setitem__((3, 6), -1),         # hole in a live row
+    lambda m: m["seq_lens"].__setitem__(1, 200),                 # more pages than the row
+    lambda m: m.__setitem__("kv_start", np.array([0, 0, 65, 0], np.int32)),
+    lambda m: m.__setitem__("kv_start", np.array([17, 0, 0, 0], np.int32)),  # no key left
+])
+def test_checker_rejects_bad_metadata(mutate):
+    st, md = _meta()
+    mutate(md)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_check_metadata(md["block_tables"], md["seq_lens"], md["query_start_loc"],
+                               md["kv_start"], st.total_q, 16, st.num_blocks)
+    assert e.value.code == pkv.PKV_E_METADATA
+
+
+def test_checker_rejects_bad_slots():
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_check_slots([0, 5, 5], 16, 4)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_check_slots([0, 64], 16, 4)
+    pkv.pkv_check_slots([-1, -1, 3, 63], 16, 4)
+
+
+def test_binding_refuses_host_tensors():
+    x = torch.zeros(4, 2, 64)
+    with pytest.raises(ValueError):
+        pkv.pkv_append(x, x, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
+                       torch.zeros(4, dtype=torch.int64))

@@ -1,0 +1,161 @@
+"""pkv_attention on the GPU against the float64 oracle over a sweep of shapes:
+group sizes 1-16, head_dim 64/128, float32 and bfloat16, decode contexts at
+page edges and across several splits, prefill chunks of 2 to 1000 tokens with
+and without cached context, mixed steps, left-padded steps; plus bitwise
+properties of the GPU path itself (physical page placement, run-to-run
+determinism, shared versus duplicated prefix pages) and a large packed step
+checked on sampled tokens.  Pools are NaN outside the valid rows."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_03_amd as pkv
+from paged_kv_attention_03_amd import workloads as W
+from tests.gpu_helpers import (check_close, gpu_attention, gpu_pools, log, oracle_seq_outputs,
+                               raw_bits)
+from tests.helpers import oracle_pools, oracle_step
+
+DTYPES = [torch.float32, torch.bfloat16]
+EDGE_LENS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 1000]
+
+
+def _run_full(st, what):
+    """GPU step vs the oracle on the whole step; also the pool bytes."""
+    q = st.make_q("cpu")
+    kp, vp = gpu_pools(st, "cpu")
+    okp, ovp = oracle_pools(st)
+    assert np.array_equal(raw_bits(kp), okp.view(raw_bits(kp).dtype)), "K pool bytes differ"
+    assert np.array_equal(raw_bits(vp), ovp.view(raw_bits(vp).dtype)), "V pool bytes differ"
+    out = gpu_attention(st, q.cuda(), kp, vp)
+    ref = oracle_step(st, q, pools=(okp, ovp))
+    check_close(out, ref, st.dtype, what)
+    return out
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 5, 8, 16])
+def test_decode_sweep(G, D, dtype):
+    log(f"decode G={G} D={D} {dtype}")
+    st = W.build_step("decode-sweep", EDGE_LENS, [1] * len(EDGE_LENS), 2 * G, 2, D, dtype,
+                      100 + G * 7 + D)
+    _run_full(st, f"decode G={G} D={D}")
+
+
+PREFILL_SHAPES = [(2, 2), (3, 10), (17, 17), (64, 100), (200, 213), (33, 1000), (1, 50),
+                  (1, 300)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 5, 8])
+def test_prefill_and_mixed_sweep(G, D, dtype):
+    log(f"prefill G={G} D={D} {dtype}")
+    ql = [a for a, _ in PREFILL_SHAPES]
+    lens = [b for _, b in PREFILL_SHAPES]
+    st = W.build_step("prefill-sweep", lens, ql, 2 * G, 2, D, dtype, 200 + G * 7 + D)
+    _run_full(st, f"prefill G={G} D={D}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+def test_left_padded_step_matches_oracle(dtype):
+    lens = [5, 40, 33, 16, 700, 1300, 260]
+    ql = [1, 2, 1, 16, 1, 100, 1]
+    st = W.build_step("padded", lens, ql, 8, 2, 128, dtype, 300, padded=True)
+    log(f"padded kv_start={st.kv_start}")
+    assert max(st.kv_start) > 1000
+    _run_full(st, "left-padded")
+
+
+@pytest.mark.gpu
+def test_page_placement_does_not_change_a_bit():
+    outs = []
+    for perm in (1, 2, 3):
+        st = W.build_step("perm", [5, 700, 33, 300], [1, 1, 20, 1], 8, 2, 128, torch.bfloat16,
+                          400, perm_seed=perm)
+        q = st.make_q("cpu").cuda()
+        kp, vp = gpu_pools(st)
+        outs.append(raw_bits(gpu_attention(st, q, kp, vp)))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.gpu
+def test_runs_are_bitwise_deterministic():
+    st = W.config_step(3)
+    q = st.make_q("cpu").cuda()
+    kp, vp = gpu_pools(st)
+    a = raw_bits(gpu_attention(st, q, kp, vp))
+    b = raw_bits(gpu_attention(st, q, kp, vp))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.gpu
+def test_shared_prefix_equals_duplicated_prefix_bitwise():
+    common = dict(steps=5, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                  prompt_lens=[600, 517, 1000, 530], shared_prefix=512)
+    runs = [W.AgentRun(**common), W.AgentRun(duplicate_prefix=True, **common)]
+    pools = []
+    for run in runs:
+        kp, vp = run.base.new_pool("cuda")
+        k, v, s = run.prefill_rows("cpu")
+        pkv.pkv_append(k.cuda(), v.cuda(), kp, vp, s.cuda())
+        pools.append((kp, vp))
+    for i in range(5):
+        outs = []
+        for run, (kp, vp) in zip(runs, pools):
+            pos, slots, bt, sl = run.step(i)
+            k, v = run.step_rows(i, "cpu")
+            pkv.pkv_append(k.cuda(), v.cuda(), kp, vp, torch.from_numpy(slots).cuda())
+            q = run.step_q(i, "cpu").cuda()
+            out = pkv.pkv_attention(q, kp, vp, torch.from_numpy(bt).cuda(),
+                                    torch.tensor(sl, dtype=torch.int32, device="cuda"),
+                                    torch.arange(5, dtype=torch.int32, device="cuda"),
+                                    run.base.scale, max_seqlen_q=1, max_seqlen_k=max(sl))
+            torch.cuda.synchronize()
+            outs.append(raw_bits(out))
+        assert np.array_equal(outs[0], outs[1]), f"step {i}"
+
+
+@pytest.mark.gpu
+def test_packed_30000_5000_10_step_on_sampled_tokens():
+    """A packed prefill step of 30,000 + 5,000 + 10 tokens (the padded-versus-
+    packed illustration of the vllm-metal post), checked on sampled tokens."""
+    lens = [30000, 5000, 10]
+    st = W.build_step("30k-5k-10", lens, lens, 8, 2, 128, torch.bfloat16, 500)
+    q = st.make_q("cpu")
+    kp, vp = gpu_pools(st, "cpu")
+    out = gpu_attention(st, q.cuda(), kp, vp)
+    qsl = st.query_start_loc()
+    toks = {0: [0, 1, 15, 16, 4095, 20000, 29999], 1: [0, 2500, 4999], 2: list(range(10))}
+    ref = oracle_seq_outputs(st, q, [0, 1, 2], "cpu", tokens=toks)
+    for s, ts in toks.items():
+        got = out[[qsl[s] + t for t in ts]]
+        check_close(got, ref[s], st.dtype, f"seq {s} tokens {ts}")
+
+
+@pytest.mark.gpu
+def test_workspace_reuse_and_explicit_out():
+    st = W.config_step(2)
+    q = st.make_q("cpu").cuda()
+    kp, vp = gpu_pools(st)
+    need = pkv.pkv_attention_workspace_size(st.num_seqs, st.total_q, st.max_seqlen_q,
+                                            st.max_seqlen_k, st.num_q_heads, st.num_kv_heads,
+                                            st.head_dim, 16, st.dtype)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    a = raw_bits(gpu_attention(st, q, kp, vp, workspace=ws, out=out))
+    b = raw_bits(gpu_attention(st, q, kp, vp, workspace=ws))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.gpu
+def test_unsupported_group_size_raises():
+    q = torch.zeros(1, 34, 128, dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_attention(q, kp, kp, torch.zeros(1, 4, **i32), torch.ones(1, **i32),
+                          torch.tensor([0, 1], **i32), 0.1, max_seqlen_q=1, max_seqlen_k=1)

@@ -306,9 +306,11 @@ MUTATIONS = {
     "no normalisation": ("o[d] /= Z;", "o[d] /= 1.0;"),
     "ignored kv_start": ("const int64_t a = kv_start ? kv_start[s] : 0;", "const int64_t a = 0;"),
     "flipped exponent": ("w[j - a] = exp(w[j - a] - m);", "w[j - a] = exp(m - w[j - a]);"),
-    "logical page as physical": (
+    # (every planted mistake keeps its reads inside the arrays it indexes)
+    "pages in reverse order": (
         "int64_t blk = block_tables[(int64_t)s * max_blocks_per_seq + j / block_size];",
-        "int64_t blk = block_tables[(int64_t)s * max_blocks_per_seq] + j / block_size;"),
+        "int64_t blk = block_tables[(int64_t)s * max_blocks_per_seq + (L - 1) / block_size"
+        " - j / block_size];"),
 }
 
 
