@@ -134,6 +134,26 @@ def time_steps(step: Step, steps: int, warmup: int, flush_bytes: int = 0):
     return wall, float(np.mean(attn)), float(np.median(attn)), float(np.min(attn))
 
 
+def device_copy_gbs(nbytes: int = 1 << 31, reps: int = 5) -> float:
+    """Bandwidth of a plain device-to-device copy of ``nbytes`` (bytes read +
+    bytes written per second): the box's practical HBM ceiling, and the
+    known-size kernel that calibrates the HBM byte counters."""
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / sec / 1e9
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -259,6 +279,8 @@ def bench_single(k, args):
     st = W.config_step(k, poison=False)
     log(f"workload {st.name}: {st.num_seqs} seqs, {sum(st.real_lens)} keys, "
         f"{kv_bytes(st) / 1e9:.3f} GB K/V")
+    copy_gbs = device_copy_gbs()
+    log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
     step = Step(st, gen_device="cuda")
     flush = 0 if k == 5 else (1 << 30)   # the large batch outgrows every cache by itself
     wall, attn_mean, attn_med, attn_min = time_steps(step, args.steps, args.warmup, flush)
@@ -279,6 +301,8 @@ def bench_single(k, args):
                    "tokens_per_step": st.total_q, "kv_bytes_per_step": kvb,
                    "cache_flush_between_steps": bool(flush)},
         "hbm_peak_frac": gbs / HBM_PEAK_GBS,
+        "device_copy_gbs": copy_gbs,
+        "copy_frac": gbs / copy_gbs,
         "packed_step_tokens_per_s": st.total_q / wall,
         "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

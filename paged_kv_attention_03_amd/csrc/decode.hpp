@@ -4,15 +4,23 @@
 // A decode step reads every visible key and value once and does a few flops
 // per byte: it is bound by memory bandwidth (vllm-metal v0.4.0 release post,
 // "The same stack on DGX Spark": decode is bandwidth-bound, prefill is
-// compute-bound).  The kernel therefore streams whole KV pages with coalesced
-// 16-byte loads, keeps everything else on chip, and spreads each sequence's
-// keys over many workgroups (split-key) so that a handful of long sequences
-// still fills the GPU; a second small kernel merges the partial results with
-// the usual log-sum-exp rescaling.
+// compute-bound).  The kernels therefore stream whole KV pages with coalesced
+// 16-byte loads and keep everything else on chip.
 //
-// Work unit: one wavefront per (sequence s, kv head g, split j).  The G query
-// heads that share kv head g are the 16 columns of a 16x16 matrix-core tile
-// (columns >= G are zero), so one pass over a page serves all of them:
+// Work split (split-key, balanced): a one-workgroup plan kernel counts the
+// page pairs of every decode sequence and cuts the list of all
+// (sequence, kv head, page pair) units into kDecodeWaves equal contiguous
+// ranges.  One persistent wavefront streams each range, crossing from one
+// (sequence, kv head) segment to the next without leaving the kernel, so every
+// wave does the same number of page pairs whatever the length mix.  A segment
+// that lies inside one wave's range is finished there and written to the
+// output; a segment cut by a range boundary leaves at most two partial results
+// per wave, which a small merge kernel combines with the usual log-sum-exp
+// rescaling.
+//
+// Per page pair, the G query heads that share kv head g are the 16 columns of
+// a 16x16 matrix-core tile (columns >= G are zero), so one pass over a page
+// serves all of them:
 //   S^T[key][head] = K_page[key][:] . q[head][:]      (MFMA, keys as rows)
 //   O^T[d][head]  += V^T[d][key] * P^T[key][head]      (MFMA, d as rows)
 // K goes straight from global memory into the A-operand registers (each lane
@@ -26,9 +34,39 @@
 // reaches the output.
 #pragma once
 
+#include <type_traits>
+
 #include "pkv_device.hpp"
 
 namespace pkv {
+
+constexpr int kDecodeWaves = 2048;     // persistent decode waves (8 per CU on 256 CUs)
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxDecodeSeqs = 16384;  // sequences the plan kernel can hold in LDS
+constexpr int kWindowPages = 256;      // block-table entries staged per window
+
+// A wave's piece of one (sequence, kv head) segment: page pairs [pi0, pi1).
+struct Portion {
+    int32_t s, g, pi0, pi1;
+    int32_t slot;          // -1: the whole segment is here, write the output;
+                           // else partial slot (wave * 2 + 0 first / 1 last piece)
+    int32_t q0;            // query row of the sequence
+    int32_t kv_lo, kv_hi;  // visible keys [kv_lo, kv_hi)
+};
+
+struct PlanParams {
+    const int32_t* seq_lens;
+    const int32_t* qsl;
+    const int32_t* kv_start;
+    int num_seqs;
+    int Hkv;
+    int max_seqlen_k;
+    int max_blocks;
+    int64_t total_q;
+    int32_t* pair_prefix;    // [num_seqs + 1] page pairs of sequences before s
+    int32_t* portion_begin;  // [kDecodeWaves + 1]
+    Portion* portions;       // [kDecodeWaves + num_seqs * Hkv]
+};
 
 struct DecodeParams {
     void* out;
@@ -36,29 +74,132 @@ struct DecodeParams {
     const void* k_pool;
     const void* v_pool;
     const int32_t* block_tables;
-    const int32_t* seq_lens;
-    const int32_t* qsl;
-    const int32_t* kv_start;
-    float* ws_o;    // [num_seqs][Hq][max_splits][D] unnormalised partial outputs
-    float* ws_ml;   // [num_seqs][Hq][max_splits][2] (running max in log2 units, sum)
-    int num_seqs;
+    const int32_t* portion_begin;
+    const Portion* portions;
+    float* ws_o;    // [kDecodeWaves * 2][G][D] unnormalised partial outputs
+    float* ws_ml;   // [kDecodeWaves * 2][G][2] (running max in log2 units, sum)
     int max_blocks;
     int Hq;
     int Hkv;
     int G;
-    int pages_per_split;
-    int max_splits;
-    int max_seqlen_k;
-    int64_t total_q;
     int64_t num_blocks;
     float scale_log2;  // softmax scale * log2(e)
 };
+
+struct MergeParams {
+    void* out;
+    const float* ws_o;
+    const float* ws_ml;
+    const int32_t* pair_prefix;
+    const int32_t* qsl;
+    int num_seqs;
+    int Hq;
+    int Hkv;
+    int G;
+};
+
+// Start of wave w's unit range, and the wave whose range holds unit u.
+__device__ __forceinline__ int64_t wave_start(int64_t w, int64_t U) { return w * U / kDecodeWaves; }
+__device__ __forceinline__ int64_t wave_of(int64_t u, int64_t U) {
+    return ((u + 1) * kDecodeWaves + U - 1) / U - 1;
+}
 
 __device__ __forceinline__ void wave_lds_fence() {
     // Orders this wave's LDS writes before its later LDS reads (and the reverse)
     // without waiting on outstanding global loads.
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+}
+
+// In-place exclusive scan of a[0..n) by a 1024-thread block; a[n] = total.
+__device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
+    const int t = threadIdx.x;
+    const int per = (n + kPlanThreads - 1) / kPlanThreads;
+    const int lo = min(n, t * per), hi = min(n, lo + per);
+    int32_t sum = 0;
+    for (int i = lo; i < hi; ++i) sum += a[i];
+    tmp[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int32_t v = t >= off ? tmp[t - off] : 0;
+        __syncthreads();
+        tmp[t] += v;
+        __syncthreads();
+    }
+    int32_t run = tmp[t] - sum;  // exclusive prefix of this thread's chunk
+    for (int i = lo; i < hi; ++i) {
+        const int32_t c = a[i];
+        a[i] = run;
+        run += c;
+    }
+    if (t == kPlanThreads - 1) a[n] = tmp[t];
+    __syncthreads();
+}
+
+// One workgroup: page pairs per decode sequence, their prefix, and every
+// wave's list of segment pieces.
+__global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(PlanParams p) {
+    __shared__ int32_t C[kMaxDecodeSeqs + 1];
+    __shared__ int32_t wcnt[kDecodeWaves + 1];
+    __shared__ int32_t tmp[kPlanThreads];
+    const int t = threadIdx.x;
+    const int S = p.num_seqs;
+    for (int s = t; s < S; s += kPlanThreads) {
+        const int q0 = p.qsl[s];
+        const bool dec = (p.qsl[s + 1] - q0 == 1) && q0 >= 0 && q0 < p.total_q;
+        const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
+        C[s] = dec ? (r.end_page - r.first_page + 1) / 2 : 0;
+    }
+    __syncthreads();
+    block_exclusive_scan(C, S, tmp);
+    const int64_t U = (int64_t)p.Hkv * C[S];
+
+    // Walks the segments that intersect wave w's range; emit=false only counts.
+    auto walk = [&](int w, bool emit, int32_t out_at) -> int {
+        const int64_t u0 = wave_start(w, U), u1 = wave_start(w + 1, U);
+        if (u0 >= u1) return 0;
+        int lo = 0, hi = S - 1;  // largest s with Hkv * C[s] <= u0 (then C[s+1] > C[s])
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)p.Hkv * C[mid] <= u0) lo = mid; else hi = mid - 1;
+        }
+        int s = lo;
+        int64_t c = C[s + 1] - C[s];
+        int g = (int)((u0 - (int64_t)p.Hkv * C[s]) / c);
+        int count = 0;
+        while (true) {
+            const int64_t seg0 = (int64_t)p.Hkv * C[s] + (int64_t)g * c;
+            const int64_t seg1 = seg0 + c;
+            if (emit) {
+                Portion q;
+                q.s = s;
+                q.g = g;
+                q.pi0 = (int32_t)(max(u0, seg0) - seg0);
+                q.pi1 = (int32_t)(min(u1, seg1) - seg0);
+                q.slot = (seg0 >= u0 && seg1 <= u1) ? -1 : w * 2 + (count == 0 ? 0 : 1);
+                q.q0 = p.qsl[s];
+                const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
+                q.kv_lo = r.a;
+                q.kv_hi = r.L;
+                p.portions[out_at + count] = q;
+            }
+            ++count;
+            if (seg1 >= u1) break;
+            if (++g == p.Hkv) {
+                g = 0;
+                do { ++s; } while (C[s + 1] == C[s]);
+                c = C[s + 1] - C[s];
+            }
+        }
+        return count;
+    };
+
+    for (int w = t; w < kDecodeWaves; w += kPlanThreads) wcnt[w] = walk(w, false, 0);
+    __syncthreads();
+    block_exclusive_scan(wcnt, kDecodeWaves, tmp);
+    for (int w = t; w < kDecodeWaves; w += kPlanThreads) walk(w, true, wcnt[w]);
+    for (int w = t; w <= kDecodeWaves; w += kPlanThreads) p.portion_begin[w] = wcnt[w];
+    for (int s = t; s <= S; s += kPlanThreads) p.pair_prefix[s] = C[s];
 }
 
 template <typename T, int D>
@@ -73,285 +214,361 @@ struct DecodeGeom {
     static constexpr int CPR = RB / 16;                // 16-B chunks per row
 };
 
+// Registers of one pair of pages in flight: K in A-operand layout, V as
+// loaded (16-byte chunks of the row-major page).
 template <typename T, int D>
-__global__ void __launch_bounds__(64) decode_kernel(DecodeParams p) {
+struct PairRegs {
+    u32x4 k[2][DecodeGeom<T, D>::KCH];
+    u32x4 v[2][DecodeGeom<T, D>::VCH];
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel(DecodeParams p) {
     using Gm = DecodeGeom<T, D>;
     constexpr bool kBF = !__is_same(T, float);
     __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * Gm::PAGE_LDS];
+    __shared__ int32_t lds_bid[kWindowPages];
 
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
-
-    int bid = blockIdx.x;
-    const int j = bid % p.max_splits;
-    bid /= p.max_splits;
-    const int g = bid % p.Hkv;
-    const int s = bid / p.Hkv;
-    if (s >= p.num_seqs) return;
-    const int q0 = p.qsl[s];
-    const int qn = p.qsl[s + 1] - q0;
-    if (qn != 1 || q0 < 0 || q0 >= p.total_q) return;
-
-    const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
-    const int npages = r.end_page - r.first_page;
-    const int P = p.pages_per_split;
-    const int nsplit = npages > 0 ? (npages + P - 1) / P : 1;
-    if (j >= nsplit) return;
-    const int pg_lo = r.first_page + j * P;
-    const int pg_hi = min(pg_lo + P, r.end_page);
-    const int kv_lo = max(r.a, pg_lo * kPage);
-    const int kv_hi = min(r.L, pg_hi * kPage);
-    const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
-    const int h = g * p.G + col;
-    const bool hvalid = col < p.G;
+    const int w = blockIdx.x;
+    const int pb = p.portion_begin[w];
+    const int pe = p.portion_begin[w + 1];
+    if (pb >= pe) return;
 
     const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
     const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
     const int64_t page_stride = (int64_t)p.Hkv * kPage * Gm::RB;  // bytes per physical page
-    const int64_t head_off = (int64_t)g * kPage * Gm::RB;
+    const bool hvalid = col < p.G;
 
-    // ---- query operand (B of S^T = K q^T): column `col`, k-slots of group `grp`
-    u32x4 qop[Gm::KCH];
-    {
-        const uint8_t* qrow = static_cast<const uint8_t*>(p.q) +
-                              ((int64_t)q0 * p.Hq + (hvalid ? h : 0)) * Gm::RB;
+    for (int b0 = pb; b0 < pe; b0 += kWave) {
+        // ---- this batch's segment pieces, one per lane
+        const int n = min(kWave, pe - b0);
+        Portion mine = {};
+        if (lane < n) mine = p.portions[b0 + lane];
+        int npairs = lane < n ? mine.pi1 - mine.pi0 : 0;
 #pragma unroll
-        for (int i = 0; i < Gm::KCH; ++i) {
-            u32x4 v = ld16(qrow + i * 64 + grp * 16);
-            qop[i] = hvalid ? v : u32x4{0, 0, 0, 0};
-        }
-    }
+        for (int off = 32; off > 0; off >>= 1) npairs += __shfl_xor(npairs, off);
+        const int K = npairs;
+        auto field = [&](int32_t v, int idx) { return __builtin_amdgcn_readlane(v, idx); };
 
-    f32x4 acc[Gm::NT];
-#pragma unroll
-    for (int t = 0; t < Gm::NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+        // ---- issue cursor (runs two pairs ahead of the process cursor)
+        int ip = 0, ipi = field(mine.pi0, 0), iend = field(mine.pi1, 0);
+        int is = field(mine.s, 0), ig = field(mine.g, 0);
+        int ifirst = field(mine.kv_lo, 0) / kPage;
+        int iendpg = (field(mine.kv_hi, 0) + kPage - 1) / kPage;
+        int wstart = -1, wseq = -1;
+        bool idone = false;
 
-    // Pages are processed two at a time (32 keys = one bf16 MFMA depth).
-    const int npair = (pg_hi - pg_lo + 1) / 2;
-    u32x4 kc[2][Gm::KCH], vc[2][Gm::VCH];
-    auto load_pair = [&](int pa, u32x4 (&kr)[2][Gm::KCH], u32x4 (&vr)[2][Gm::VCH]) {
+        auto issue = [&](PairRegs<T, D>& R) {
+            const int pa = ifirst + 2 * ipi;
+            const int pb2 = (pa + 1 < iendpg) ? pa + 1 : pa;
+            if (wseq != is || pa < wstart || pb2 >= wstart + kWindowPages) {
+                // stage the next window of this sequence's block-table row
+                const int32_t* bt = p.block_tables + (int64_t)is * p.max_blocks;
+                int32_t ids[kWindowPages / kWave];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int pg = (pa + x < pg_hi) ? pa + x : pa;
-            const int64_t blk = safe_block(bt, pg, p.num_blocks);
-            const uint8_t* kb = kpool + blk * page_stride + head_off;
-            const uint8_t* vb = vpool + blk * page_stride + head_off;
+                for (int c = 0; c < kWindowPages / kWave; ++c) {
+                    const int pg = pa + c * kWave + lane;
+                    ids[c] = pg < iendpg ? bt[pg] : 0;
+                }
+                wave_lds_fence();
 #pragma unroll
-            for (int i = 0; i < Gm::KCH; ++i) kr[x][i] = ld16(kb + col * Gm::RB + i * 64 + grp * 16);
-#pragma unroll
-            for (int c = 0; c < Gm::VCH; ++c) vr[x][c] = ld16(vb + (c * kWave + lane) * 16);
-        }
-    };
-    auto stage_v = [&](const u32x4 (&vr)[2][Gm::VCH]) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int c = 0; c < Gm::VCH; ++c) {
-                const int ci = c * kWave + lane;
-                const int row = ci / Gm::CPR, cc = ci % Gm::CPR;
-                st16(lds_v + x * Gm::PAGE_LDS + row * Gm::RS + cc * 16, vr[x][c]);
+                for (int c = 0; c < kWindowPages / kWave; ++c)
+                    lds_bid[c * kWave + lane] =
+                        (ids[c] >= 0 && ids[c] < p.num_blocks) ? ids[c] : 0;
+                wave_lds_fence();
+                wstart = pa;
+                wseq = is;
             }
-    };
-
-    if (npair > 0) {
-        load_pair(pg_lo, kc, vc);
-        stage_v(vc);
-    }
-    for (int it = 0; it < npair; ++it) {
-        const int pa = pg_lo + 2 * it;
-        const bool more = it + 1 < npair;
-        u32x4 kn[2][Gm::KCH], vn[2][Gm::VCH];
-        if (more) load_pair(pa + 2, kn, vn);
-        wave_lds_fence();
-
-        // ---- logits for 2 pages: lane holds keys 4*grp+{0..3} of each page, column col
-        f32x4 sx[2];
+            const int64_t head_off = (int64_t)ig * kPage * Gm::RB;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (kBF) {
-#pragma unroll
-                for (int i = 0; i < Gm::KCH; ++i) sacc = mfma_bf16(kc[x][i], qop[i], sacc);
-            } else {
+            for (int x = 0; x < 2; ++x) {
+                const int pg = x ? pb2 : pa;
+                const int64_t blk = __builtin_amdgcn_readfirstlane(lds_bid[pg - wstart]);
+                const uint8_t* kb = kpool + blk * page_stride + head_off;
+                const uint8_t* vb = vpool + blk * page_stride + head_off;
 #pragma unroll
                 for (int i = 0; i < Gm::KCH; ++i)
+                    R.k[x][i] = ld16(kb + col * Gm::RB + i * 64 + grp * 16);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        sacc = mfma_f32(__uint_as_float(kc[x][i][t]), __uint_as_float(qop[i][t]),
-                                        sacc);
+                for (int c = 0; c < Gm::VCH; ++c) R.v[x][c] = ld16(vb + (c * kWave + lane) * 16);
             }
-            sx[x] = sacc;
-        }
-        const bool edge = (pa * kPage < kv_lo) || ((pa + 2) * kPage > kv_hi);
-        float sv[8];
-        bool valid[8];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int key = (pa + x) * kPage + grp * 4 + t;
-                valid[x * 4 + t] = !edge || (key >= kv_lo && key < kv_hi);
-                sv[x * 4 + t] = valid[x * 4 + t] ? sx[x][t] * p.scale_log2 : -INFINITY;
-            }
-        float mt = sv[0];
-#pragma unroll
-        for (int t = 1; t < 8; ++t) mt = fmaxf(mt, sv[t]);
-        mt = col_max(mt);
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        float pv[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            pv[t] = fast_exp2(sv[t] - m_use);
-            psum += pv[t];
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int t = 0; t < Gm::NT; ++t) acc[t] *= alpha;
-
-        // ---- O^T += V^T P^T, V^T gathered from the staged pages
-        if constexpr (kBF) {
-            u32x4 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
-                        pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
-            const uint16_t* l16 = reinterpret_cast<const uint16_t*>(lds_v);
-#pragma unroll
-            for (int t = 0; t < Gm::NT; ++t) {
-                const int d = t * 16 + col;
-                u32x4 a;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int x = w >> 1;
-                    const int k0 = grp * 4 + (w & 1) * 2;
-                    const int base = (x * Gm::PAGE_LDS + k0 * Gm::RS) / 2 + d;
-                    uint32_t lo = l16[base];
-                    uint32_t hi = l16[base + Gm::RS / 2];
-                    if (edge) {
-                        lo = valid[2 * w] ? lo : 0u;
-                        hi = valid[2 * w + 1] ? hi : 0u;
-                    }
-                    a[w] = lo | (hi << 16);
+            // advance; past the end the last pair is loaded again (cache hit, unused)
+            if (!idone && ++ipi == iend) {
+                if (ip + 1 < n) {
+                    ++ip;
+                    ipi = field(mine.pi0, ip);
+                    iend = field(mine.pi1, ip);
+                    is = field(mine.s, ip);
+                    ig = field(mine.g, ip);
+                    ifirst = field(mine.kv_lo, ip) / kPage;
+                    iendpg = (field(mine.kv_hi, ip) + kPage - 1) / kPage;
+                } else {
+                    idone = true;
+                    --ipi;
                 }
-                acc[t] = mfma_bf16(a, pb, acc[t]);
             }
-        } else {
-            const float* lf = reinterpret_cast<const float*>(lds_v);
+        };
+
+        // ---- process cursor state: the segment piece being accumulated
+        int pp = -1, ppi = 0, pend = 0;
+        int ps = 0, pg_ = 0, pslot = 0, pq0 = 0, plo = 0, phi = 0, pfirst = 0;
+        u32x4 qop[Gm::KCH];
+        f32x4 acc[Gm::NT];
+        float m_run = -INFINITY, l_run = 0.f;
+
+        auto begin_piece = [&](int idx) {
+            pp = idx;
+            ppi = field(mine.pi0, idx);
+            pend = field(mine.pi1, idx);
+            ps = field(mine.s, idx);
+            pg_ = field(mine.g, idx);
+            pslot = field(mine.slot, idx);
+            pq0 = field(mine.q0, idx);
+            plo = field(mine.kv_lo, idx);
+            phi = field(mine.kv_hi, idx);
+            pfirst = plo / kPage;
+            const int h = pg_ * p.G + col;
+            const uint8_t* qrow = static_cast<const uint8_t*>(p.q) +
+                                  ((int64_t)pq0 * p.Hq + (hvalid ? h : 0)) * Gm::RB;
+#pragma unroll
+            for (int i = 0; i < Gm::KCH; ++i) {
+                u32x4 v = ld16(qrow + i * 64 + grp * 16);
+                qop[i] = hvalid ? v : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int t = 0; t < Gm::NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run = -INFINITY;
+            l_run = 0.f;
+        };
+
+        auto finish_piece = [&]() {
+            const float l_tot = col_sum(l_run);
+            if (!hvalid) return;
+            const int h = pg_ * p.G + col;
+            if (pslot < 0) {
+                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                uint8_t* orow = static_cast<uint8_t*>(p.out) + ((int64_t)pq0 * p.Hq + h) * Gm::RB;
+#pragma unroll
+                for (int t = 0; t < Gm::NT; ++t) {
+                    const int d = t * 16 + grp * 4;
+                    if constexpr (kBF) {
+                        uint32_t w0 = pack_bf16(acc[t][0] * inv, acc[t][1] * inv);
+                        uint32_t w1 = pack_bf16(acc[t][2] * inv, acc[t][3] * inv);
+                        *reinterpret_cast<uint2*>(orow + d * 2) = make_uint2(w0, w1);
+                    } else {
+                        *reinterpret_cast<f32x4*>(orow + d * 4) = acc[t] * inv;
+                    }
+                }
+            } else {
+                const int64_t slot = (int64_t)pslot * p.G + col;
+                float* o = p.ws_o + slot * D;
+#pragma unroll
+                for (int t = 0; t < Gm::NT; ++t)
+                    *reinterpret_cast<f32x4*>(o + t * 16 + grp * 4) = acc[t];
+                if (grp == 0) {
+                    p.ws_ml[slot * 2] = m_run;
+                    p.ws_ml[slot * 2 + 1] = l_tot;
+                }
+            }
+        };
+
+        // One pair of pages.  `edge` pairs (partly outside [kv_lo, kv_hi)) mask
+        // keys and zero their V entries; interior pairs skip all masking.  The
+        // running max is raised lazily: only when a tile's max exceeds it by
+        // more than 8 (log2 units), so probabilities stay below 2^8 and the
+        // accumulator rescale is rare.
+        auto process = [&](auto edge_tag, int pa, const PairRegs<T, D>& R) {
+            constexpr bool EDGE = decltype(edge_tag)::value;
+            const int kv_lo = plo, kv_hi = phi;
+            // stage V (row-major, padded rows) for the transposed reads below
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int key = grp * 4 + u;
-                    const bool ok = valid[x * 4 + u];
-#pragma unroll
-                    for (int t = 0; t < Gm::NT; ++t) {
-                        float v = lf[(x * Gm::PAGE_LDS + key * Gm::RS) / 4 + t * 16 + col];
-                        v = ok ? v : 0.f;
-                        acc[t] = mfma_f32(v, pv[x * 4 + u], acc[t]);
-                    }
+                for (int c = 0; c < Gm::VCH; ++c) {
+                    const int ci = c * kWave + lane;
+                    const int row = ci / Gm::CPR, cc = ci % Gm::CPR;
+                    st16(lds_v + x * Gm::PAGE_LDS + row * Gm::RS + cc * 16, R.v[x][c]);
                 }
-        }
-        wave_lds_fence();
-        if (more) {
+            wave_lds_fence();
+
+            // logits: lane holds keys 4*grp+{0..3} of each page for column col
+            f32x4 sx[2];
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
+                f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (kBF) {
 #pragma unroll
-                for (int i = 0; i < Gm::KCH; ++i) kc[x][i] = kn[x][i];
+                    for (int i = 0; i < Gm::KCH; ++i) sacc = mfma_bf16(R.k[x][i], qop[i], sacc);
+                } else {
 #pragma unroll
-                for (int c = 0; c < Gm::VCH; ++c) vc[x][c] = vn[x][c];
+                    for (int i = 0; i < Gm::KCH; ++i)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            sacc = mfma_f32(__uint_as_float(R.k[x][i][t]),
+                                            __uint_as_float(qop[i][t]), sacc);
+                }
+                sx[x] = sacc;
             }
-            stage_v(vc);
-        }
-    }
+            float sv[8];
+            bool valid[8];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int key = (pa + x) * kPage + grp * 4 + t;
+                    valid[x * 4 + t] =
+                        !EDGE || (unsigned)(key - kv_lo) < (unsigned)(kv_hi - kv_lo);
+                    sv[x * 4 + t] = valid[x * 4 + t] ? sx[x][t] * p.scale_log2 : -INFINITY;
+                }
+            float mt = sv[0];
+#pragma unroll
+            for (int t = 1; t < 8; ++t) mt = fmaxf(mt, sv[t]);
+            mt = col_max(mt);
+            if (__any(mt > m_run + 8.f)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run - m_use);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < Gm::NT; ++t) acc[t] *= alpha;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            float pv[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                pv[t] = fast_exp2(sv[t] - m_use);
+                psum += pv[t];
+            }
+            l_run += psum;
 
-    const float l_tot = col_sum(l_run);
-    if (!hvalid) return;
-    if (nsplit == 1) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint8_t* orow = static_cast<uint8_t*>(p.out) + ((int64_t)q0 * p.Hq + h) * Gm::RB;
-#pragma unroll
-        for (int t = 0; t < Gm::NT; ++t) {
-            const int d = t * 16 + grp * 4;
+            // O^T += V^T P^T, V^T gathered from the staged pages
             if constexpr (kBF) {
-                uint32_t w0 = pack_bf16(acc[t][0] * inv, acc[t][1] * inv);
-                uint32_t w1 = pack_bf16(acc[t][2] * inv, acc[t][3] * inv);
-                *reinterpret_cast<uint2*>(orow + d * 2) = make_uint2(w0, w1);
-            } else {
-                *reinterpret_cast<f32x4*>(orow + d * 4) = acc[t] * inv;
-            }
-        }
-    } else {
-        const int64_t slot = ((int64_t)s * p.Hq + h) * p.max_splits + j;
-        float* o = p.ws_o + slot * D;
+                u32x4 pbv = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
+                             pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
+                const uint16_t* l16 = reinterpret_cast<const uint16_t*>(lds_v);
+                uint32_t keep[4];
 #pragma unroll
-        for (int t = 0; t < Gm::NT; ++t)
-            *reinterpret_cast<f32x4*>(o + t * 16 + grp * 4) = acc[t];
-        if (grp == 0) {
-            p.ws_ml[slot * 2] = m_run;
-            p.ws_ml[slot * 2 + 1] = l_tot;
+                for (int q = 0; q < 4; ++q)
+                    keep[q] = (valid[2 * q] ? 0x0000ffffu : 0u) |
+                              (valid[2 * q + 1] ? 0xffff0000u : 0u);
+#pragma unroll
+                for (int t = 0; t < Gm::NT; ++t) {
+                    const int d = t * 16 + col;
+                    u32x4 a;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int x = q >> 1;
+                        const int k0 = grp * 4 + (q & 1) * 2;
+                        const int base = (x * Gm::PAGE_LDS + k0 * Gm::RS) / 2 + d;
+                        a[q] = (uint32_t)l16[base] | ((uint32_t)l16[base + Gm::RS / 2] << 16);
+                        if constexpr (EDGE) a[q] &= keep[q];
+                    }
+                    acc[t] = mfma_bf16(a, pbv, acc[t]);
+                }
+            } else {
+                const float* lf = reinterpret_cast<const float*>(lds_v);
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int key = grp * 4 + u;
+#pragma unroll
+                        for (int t = 0; t < Gm::NT; ++t) {
+                            float v = lf[(x * Gm::PAGE_LDS + key * Gm::RS) / 4 + t * 16 + col];
+                            if constexpr (EDGE) v = valid[x * 4 + u] ? v : 0.f;
+                            acc[t] = mfma_f32(v, pv[x * 4 + u], acc[t]);
+                        }
+                    }
+            }
+            wave_lds_fence();
+        };
+
+        auto consume = [&](const PairRegs<T, D>& R) {
+            if (pp < 0 || ppi == pend) {
+                if (pp >= 0) finish_piece();
+                begin_piece(pp + 1);
+            }
+            const int pa = pfirst + 2 * ppi;
+            if ((pa * kPage < plo) || ((pa + 2) * kPage > phi))
+                process(std::true_type{}, pa, R);
+            else
+                process(std::false_type{}, pa, R);
+            ++ppi;
+        };
+
+        if (K > 0) {
+            PairRegs<T, D> A, B;
+            issue(A);
+            issue(B);
+            for (int k = 0; k < K; k += 2) {
+                consume(A);
+                issue(A);
+                if (k + 1 < K) consume(B);
+                issue(B);
+            }
+            finish_piece();
         }
     }
 }
 
-struct MergeParams {
-    void* out;
-    const float* ws_o;
-    const float* ws_ml;
-    const int32_t* seq_lens;
-    const int32_t* qsl;
-    const int32_t* kv_start;
-    int num_seqs;
-    int max_blocks;
-    int Hq;
-    int pages_per_split;
-    int max_splits;
-    int max_seqlen_k;
-    int64_t total_q;
-};
-
-// One wavefront per (sequence, query head): out = sum_j 2^(m_j - M) o_j /
-// sum_j 2^(m_j - M) l_j, rounded to the output type.
+// One wavefront per (sequence, query head) whose segment was cut by a wave
+// boundary: out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over its
+// pieces, rounded to the output type.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) merge_kernel(MergeParams p) {
     constexpr bool kBF = !__is_same(T, float);
     const int h = blockIdx.x % p.Hq;
     const int s = blockIdx.x / p.Hq;
     if (s >= p.num_seqs) return;
-    const int q0 = p.qsl[s];
-    if (p.qsl[s + 1] - q0 != 1 || q0 < 0 || q0 >= p.total_q) return;
-    const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
-    const int npages = r.end_page - r.first_page;
-    const int nsplit = npages > 0 ? (npages + p.pages_per_split - 1) / p.pages_per_split : 1;
-    if (nsplit <= 1) return;
-    const int64_t base = ((int64_t)s * p.Hq + h) * p.max_splits;
+    const int64_t c = p.pair_prefix[s + 1] - p.pair_prefix[s];
+    if (c <= 0) return;
+    const int64_t U = (int64_t)p.Hkv * p.pair_prefix[p.num_seqs];
+    const int g = h / p.G, col = h - (h / p.G) * p.G;
+    const int64_t a = (int64_t)p.Hkv * p.pair_prefix[s] + g * c;
+    const int64_t wa = wave_of(a, U), wb = wave_of(a + c - 1, U);
+    if (wa == wb) return;  // the wave that holds the whole segment wrote it
+    auto slot_of = [&](int64_t w) {
+        const int which = (w == wa && wave_start(wa, U) != a) ? 1 : 0;
+        return (w * 2 + which) * p.G + col;
+    };
+    // The waves holding the segment's units, each visited once: when there are
+    // fewer units than waves, waves with empty ranges lie between them.
+    const int64_t seg_end = a + c;
     float M = -INFINITY;
-    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, p.ws_ml[(base + j) * 2]);
+    for (int64_t u = a; u < seg_end;) {
+        const int64_t w = wave_of(u, U);
+        M = fmaxf(M, p.ws_ml[slot_of(w) * 2]);
+        u = wave_start(w + 1, U);
+    }
     const float Mu = (M == -INFINITY) ? 0.f : M;
     constexpr int PER = D / kWave;  // output elements per lane (1 or 2)
     float num[PER], den = 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) num[e] = 0.f;
-    for (int j = 0; j < nsplit; ++j) {
-        const float w = fast_exp2(p.ws_ml[(base + j) * 2] - Mu);
-        den += w * p.ws_ml[(base + j) * 2 + 1];
-        const float* o = p.ws_o + (base + j) * D;
+    for (int64_t u = a; u < seg_end;) {
+        const int64_t w = wave_of(u, U);
+        u = wave_start(w + 1, U);
+        const int64_t sl = slot_of(w);
+        const float wt = fast_exp2(p.ws_ml[sl * 2] - Mu);
+        den += wt * p.ws_ml[sl * 2 + 1];
+        const float* o = p.ws_o + sl * D;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += w * o[threadIdx.x * PER + e];
+        for (int e = 0; e < PER; ++e) num[e] += wt * o[threadIdx.x * PER + e];
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     uint8_t* orow = static_cast<uint8_t*>(p.out) +
-                    ((int64_t)q0 * p.Hq + h) * (int64_t)D * Elem<T>::kBytes;
+                    ((int64_t)p.qsl[s] * p.Hq + h) * (int64_t)D * Elem<T>::kBytes;
     if constexpr (kBF) {
         if constexpr (PER == 2) {
             reinterpret_cast<uint32_t*>(orow)[threadIdx.x] = pack_bf16(num[0] * inv, num[1] * inv);
         } else {
-            bf16x2 v = {(__bf16)(num[0] * inv), (__bf16)0.f};
             reinterpret_cast<uint16_t*>(orow)[threadIdx.x] =
-                (uint16_t)(__builtin_bit_cast(uint32_t, v) & 0xffffu);
+                (uint16_t)(pack_bf16(num[0] * inv, 0.f) & 0xffffu);
         }
     } else {
 #pragma unroll

@@ -58,48 +58,36 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 // ---------------------------------------------------------------- planner
 
+// Workspace layout (every region 256-byte aligned):
+//   pair_prefix   int32[num_seqs + 1]          page pairs of decode sequences before s
+//   portion_begin int32[kDecodeWaves + 1]      each wave's first segment piece
+//   portions      Portion[kDecodeWaves + num_seqs * Hkv]
+//   ws_o          float[kDecodeWaves * 2][G][D] partial outputs of cut segments
+//   ws_ml         float[kDecodeWaves * 2][G][2] their running max and sum
 struct Plan {
-    int pages_per_split = 1;
-    int max_splits = 1;
+    size_t off_prefix = 0, off_pbegin = 0, off_portions = 0, off_o = 0, off_ml = 0, total = 0;
     int prefill_tile_tokens = 0;
-    size_t ws_o_bytes = 0;
-    size_t ws_ml_bytes = 0;
-    size_t ws_bytes() const { return ws_o_bytes + ws_ml_bytes; }
 };
 
 constexpr int kBlock = 16;
-// Decode workgroups the planner aims for: enough single-wavefront workgroups
-// to keep every CU of an MI355X (256 CUs, several waves each) streaming pages.
-constexpr long kDecodeTargetWG = 16384;
 
-int env_int(const char* name, int dflt) {
-    const char* v = std::getenv(name);
-    if (!v || !*v) return dflt;
-    return std::atoi(v);
-}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Plan make_plan(int num_seqs, int max_seqlen_k, int num_q_heads, int num_kv_heads,
-               int head_dim, int group) {
+Plan make_plan(int num_seqs, int num_kv_heads, int head_dim, int group) {
     Plan pl;
-    const long max_pages = (max_seqlen_k + kBlock - 1) / kBlock;
-    // Units of (sequence, kv head) times pages, spread over the target number of
-    // workgroups; an even split keeps whole page pairs per workgroup.
-    long est = (long)num_seqs * num_kv_heads * max_pages;
-    long pps = (est + kDecodeTargetWG - 1) / kDecodeTargetWG;
-    if (pps < 8) pps = 8;
-    if (pps > 512) pps = 512;
-    pps = (pps + 1) & ~1L;
-    const int forced = env_int("PKV_DECODE_PAGES_PER_SPLIT", 0);
-    if (forced > 0) pps = (forced + 1) & ~1;
-    pl.pages_per_split = (int)pps;
-    pl.max_splits = (int)((max_pages + pps - 1) / pps);
-    if (pl.max_splits < 1) pl.max_splits = 1;
+    size_t off = 0;
+    pl.off_prefix = off;
+    off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
+    pl.off_pbegin = off;
+    off = align256(off + sizeof(int32_t) * (size_t)(pkv::kDecodeWaves + 1));
+    pl.off_portions = off;
+    off = align256(off + sizeof(pkv::Portion) * ((size_t)pkv::kDecodeWaves + (size_t)num_seqs * num_kv_heads));
+    pl.off_o = off;
+    off = align256(off + sizeof(float) * (size_t)pkv::kDecodeWaves * 2 * group * head_dim);
+    pl.off_ml = off;
+    off = align256(off + sizeof(float) * (size_t)pkv::kDecodeWaves * 2 * group * 2);
+    pl.total = off;
     pl.prefill_tile_tokens = pkv::kPrefillRows / group;
-    if (pl.max_splits > 1) {
-        const size_t slots = (size_t)num_seqs * num_q_heads * pl.max_splits;
-        pl.ws_o_bytes = slots * head_dim * sizeof(float);
-        pl.ws_ml_bytes = slots * 2 * sizeof(float);
-    }
     return pl;
 }
 
@@ -123,17 +111,16 @@ int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size
 }
 
 template <typename T, int D>
-int launch_attention(const pkv::DecodeParams& dp, const pkv::MergeParams& mp,
-                     const pkv::PrefillParams& pp, int max_seqlen_q, int64_t total_q, int num_seqs,
-                     hipStream_t stream) {
-    const long dgrid = (long)dp.max_splits * dp.Hkv * num_seqs;
-    hipLaunchKernelGGL((pkv::decode_kernel<T, D>), dim3((unsigned)dgrid), dim3(64), 0, stream, dp);
+int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
+                     const pkv::MergeParams& mp, const pkv::PrefillParams& pp, int max_seqlen_q,
+                     int64_t total_q, int num_seqs, hipStream_t stream) {
+    hipLaunchKernelGGL(pkv::decode_plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, stream, pl);
+    if (int rc = hip_status("decode plan launch")) return rc;
+    hipLaunchKernelGGL((pkv::decode_kernel<T, D>), dim3(pkv::kDecodeWaves), dim3(64), 0, stream, dp);
     if (int rc = hip_status("decode launch")) return rc;
-    if (dp.max_splits > 1) {
-        hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)),
-                           dim3(64), 0, stream, mp);
-        if (int rc = hip_status("merge launch")) return rc;
-    }
+    hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)), dim3(64),
+                       0, stream, mp);
+    if (int rc = hip_status("merge launch")) return rc;
     if (max_seqlen_q > 1) {
         const long tiles = (total_q + pp.tile_tokens - 1) / pp.tile_tokens + num_seqs;
         hipLaunchKernelGGL((pkv::prefill_kernel<T, D>), dim3((unsigned)tiles, pp.Hkv),
@@ -197,13 +184,12 @@ size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqle
                                     int head_dim, int block_size, pkv_dtype_t dtype) {
     (void)total_q;
     (void)max_seqlen_q;
+    (void)max_seqlen_k;
     (void)dtype;
-    if (num_seqs <= 0 || max_seqlen_k <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-        head_dim <= 0 || block_size != kBlock || num_q_heads % num_kv_heads)
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size != kBlock || num_q_heads % num_kv_heads)
         return 0;
-    return make_plan(num_seqs, max_seqlen_k, num_q_heads, num_kv_heads, head_dim,
-                     num_q_heads / num_kv_heads)
-        .ws_bytes();
+    return make_plan(num_seqs, num_kv_heads, head_dim, num_q_heads / num_kv_heads).total;
 }
 
 int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -240,20 +226,37 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
         overlaps(out, io_bytes, v_pool, pool_bytes))
         return fail(PKV_E_ARG, "out must not alias q or the pools");
 
+    if (num_seqs > pkv::kMaxDecodeSeqs)
+        return fail(PKV_E_UNSUPPORTED, "num_seqs %d > %d is not supported", num_seqs,
+                    pkv::kMaxDecodeSeqs);
     const int G = num_q_heads / num_kv_heads;
-    const Plan pl = make_plan(num_seqs, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, G);
-    if (pl.ws_bytes() > 0) {
-        if (!workspace || workspace_bytes < pl.ws_bytes())
-            return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                        workspace ? workspace_bytes : (size_t)0, pl.ws_bytes());
-        if (!aligned16(workspace)) return fail(PKV_E_ARG, "workspace must be 16-byte aligned");
-        if (overlaps(workspace, pl.ws_bytes(), out, io_bytes))
-            return fail(PKV_E_ARG, "workspace must not alias out");
-    }
+    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, G);
+    if (!workspace || workspace_bytes < pl.total)
+        return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace ? workspace_bytes : (size_t)0, pl.total);
+    if (!aligned16(workspace)) return fail(PKV_E_ARG, "workspace must be 16-byte aligned");
+    if (overlaps(workspace, pl.total, out, io_bytes))
+        return fail(PKV_E_ARG, "workspace must not alias out");
     const float scale_log2 = scale * 1.4426950408889634f;
-    float* ws_o = pl.ws_bytes() ? static_cast<float*>(workspace) : nullptr;
-    float* ws_ml = pl.ws_bytes() ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes)
-                                 : nullptr;
+    char* wsb = static_cast<char*>(workspace);
+    int32_t* prefix = reinterpret_cast<int32_t*>(wsb + pl.off_prefix);
+    int32_t* pbegin = reinterpret_cast<int32_t*>(wsb + pl.off_pbegin);
+    pkv::Portion* portions = reinterpret_cast<pkv::Portion*>(wsb + pl.off_portions);
+    float* ws_o = reinterpret_cast<float*>(wsb + pl.off_o);
+    float* ws_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
+
+    pkv::PlanParams plp;
+    plp.seq_lens = seq_lens;
+    plp.qsl = query_start_loc;
+    plp.kv_start = kv_start;
+    plp.num_seqs = num_seqs;
+    plp.Hkv = num_kv_heads;
+    plp.max_seqlen_k = max_seqlen_k;
+    plp.max_blocks = max_blocks_per_seq;
+    plp.total_q = total_q;
+    plp.pair_prefix = prefix;
+    plp.portion_begin = pbegin;
+    plp.portions = portions;
 
     pkv::DecodeParams dp;
     dp.out = out;
@@ -261,20 +264,14 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     dp.k_pool = k_pool;
     dp.v_pool = v_pool;
     dp.block_tables = block_tables;
-    dp.seq_lens = seq_lens;
-    dp.qsl = query_start_loc;
-    dp.kv_start = kv_start;
+    dp.portion_begin = pbegin;
+    dp.portions = portions;
     dp.ws_o = ws_o;
     dp.ws_ml = ws_ml;
-    dp.num_seqs = num_seqs;
     dp.max_blocks = max_blocks_per_seq;
     dp.Hq = num_q_heads;
     dp.Hkv = num_kv_heads;
     dp.G = G;
-    dp.pages_per_split = pl.pages_per_split;
-    dp.max_splits = pl.max_splits;
-    dp.max_seqlen_k = max_seqlen_k;
-    dp.total_q = total_q;
     dp.num_blocks = num_blocks;
     dp.scale_log2 = scale_log2;
 
@@ -282,16 +279,12 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     mp.out = out;
     mp.ws_o = ws_o;
     mp.ws_ml = ws_ml;
-    mp.seq_lens = seq_lens;
+    mp.pair_prefix = prefix;
     mp.qsl = query_start_loc;
-    mp.kv_start = kv_start;
     mp.num_seqs = num_seqs;
-    mp.max_blocks = max_blocks_per_seq;
     mp.Hq = num_q_heads;
-    mp.pages_per_split = pl.pages_per_split;
-    mp.max_splits = pl.max_splits;
-    mp.max_seqlen_k = max_seqlen_k;
-    mp.total_q = total_q;
+    mp.Hkv = num_kv_heads;
+    mp.G = G;
 
     pkv::PrefillParams pp;
     pp.out = out;
@@ -313,16 +306,14 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     pp.num_blocks = num_blocks;
     pp.scale_log2 = scale_log2;
 
-    const long dgrid = (long)pl.max_splits * num_kv_heads * num_seqs;
-    if (dgrid > 0x7fffffffL) return fail(PKV_E_ARG, "decode grid too large");
     hipStream_t st = static_cast<hipStream_t>(stream);
     int rc;
     if (dtype == PKV_BF16)
-        rc = head_dim == 128 ? launch_attention<pkv::bf16_t, 128>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
-                             : launch_attention<pkv::bf16_t, 64>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
+        rc = head_dim == 128 ? launch_attention<pkv::bf16_t, 128>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
+                             : launch_attention<pkv::bf16_t, 64>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
     else
-        rc = head_dim == 128 ? launch_attention<float, 128>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
-                             : launch_attention<float, 64>(dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
+        rc = head_dim == 128 ? launch_attention<float, 128>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
+                             : launch_attention<float, 64>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
     if (rc) return rc;
     return ok();
 }

@@ -62,6 +62,7 @@ def _attn(lib, **over):
     (dict(nb=0), pkv.PKV_E_ARG),
     (dict(num_seqs=-1), pkv.PKV_E_ARG),
     (dict(scale=float("nan")), pkv.PKV_E_ARG),
+    (dict(num_seqs=16385, total_q=16385, max_blocks=8), pkv.PKV_E_UNSUPPORTED),
 ])
 def test_attention_rejects_invalid_arguments(lib, over, code):
     assert _attn(lib, **over) == code
@@ -86,9 +87,11 @@ def test_empty_steps_launch_nothing(lib):
 def test_workspace_size_follows_the_plan(lib):
     ws = lambda ns, msk, hq=16, hkv=8, d=128: lib.pkv_attention_workspace_size(
         ns, ns, 1, msk, hq, hkv, d, 16, pkv.PKV_BF16)
-    assert ws(4, 100, 4, 2, 64) == 0           # a short context needs one split
+    small = ws(4, 100, 4, 2, 64)
     big = ws(128, 32768, 64, 8)
-    assert big > 0 and big % 16 == 0
+    assert 0 < small < big and big % 256 == 0
+    assert ws(128, 100, 64, 8) == big          # independent of context length
+    assert ws(256, 100, 64, 8) > big           # grows with the batch
     assert ws(0, 100) == 0
     assert lib.pkv_attention_workspace_size(4, 4, 1, 100, 4, 2, 64, 32, pkv.PKV_BF16) == 0
 
