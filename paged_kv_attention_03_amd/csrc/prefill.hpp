@@ -13,12 +13,23 @@
 // Work unit: one workgroup of four wavefronts per (sequence, kv head, tile of
 // query tokens).  The G query heads of the kv head are folded into the tile's
 // rows (row = token * G + head), so every staged K/V page serves all of them.
-// Each wavefront owns 32 rows (two 16-column MFMA tiles).  Pairs of KV pages
-// (32 keys) are staged in LDS once per workgroup, double-buffered, and read by
-// all four wavefronts.  The sequence that owns a tile is found by a binary
-// search over query_start_loc ("Replacing attention, reusing the rest": each
-// threadgroup finds its request by binary search over cu_seqlens).
+// Each wavefront owns 32 rows (two 16-column MFMA tiles), keys being the MFMA
+// rows:  S^T = K q^T,  O^T += V^T P^T.
+//
+// Staging: pairs of KV pages (32 keys; K and V of two pages, 16 KiB for bf16
+// head_dim 128) go from HBM straight into a ring of kStages LDS buffers with
+// global->LDS loads, kStages - 1 pairs ahead of the pair being consumed, one
+// barrier per pair.  Inside a buffer each 16-byte chunk of a row sits at
+// chunk ^ f(row), so the 16 key rows read for one K operand fall in distinct
+// banks.  V^T operands come from the transposing LDS read (ds_read_b64_tr_b16),
+// which hands each lane 4 consecutive keys of one column.  The workgroup's
+// block-table entries are staged in LDS once.  The sequence that owns a tile
+// is found by a binary search over query_start_loc ("Replacing attention,
+// reusing the rest": each threadgroup finds its request by binary search over
+// cu_seqlens).
 #pragma once
+
+#include <type_traits>
 
 #include "pkv_device.hpp"
 
@@ -47,33 +58,82 @@ struct PrefillParams {
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = 32 * kPrefillWaves;
+constexpr int kMaxPrefillPages = 4096;  // block-table entries a workgroup stages (64K keys)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// 16 bytes from global memory straight into LDS: lane l writes block + 16 * l.
+__device__ __forceinline__ void load_to_lds16(const void* g, uint8_t* block) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)block, 16, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// (i % 4) of the 4 consecutive 16-bit values that lane 4r + i / 4 points at,
+// for r = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* addr) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)addr);
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): a fence
+// would make the compiler wait for every global->LDS load in flight, including
+// the stages loaded ahead.  Visibility of a stage is ensured by the explicit
+// vmcnt wait that precedes this barrier; the empty asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_keep_loads_in_flight() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) left free
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <typename T, int D>
 struct PrefillGeom {
     static constexpr int EB = Elem<T>::kBytes;
-    static constexpr int RB = D * EB;
-    static constexpr int RS = RB + 16;
-    static constexpr int PAGE_LDS = kPage * RS;
-    static constexpr int STAGE = 4 * PAGE_LDS;          // K page a, K page b, V page a, V page b
+    static constexpr int RB = D * EB;                    // bytes per K/V row
+    static constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+    static constexpr int PAGE = kPage * RB;              // bytes of one (page, head)
+    static constexpr int BLOCKS = 4 * PAGE / 1024;       // 1 KiB load blocks per stage
+    static constexpr int LPT = BLOCKS / kPrefillWaves;   // load instructions per thread
+    static constexpr int ROWS_PER_BLOCK = 1024 / RB;
+    static constexpr int STAGE = 4 * PAGE;               // K a, K b, V a, V b
+    static constexpr int kStages = (STAGE <= 16384) ? 4 : 2;
     static constexpr int NT = D / 16;
     static constexpr int KCH = RB / 64;
-    static constexpr int CPR = RB / 16;
-    static constexpr int LCH = 4 * kPage * CPR / (kPrefillWaves * kWave);  // chunks per thread per stage
 };
+
+// Chunk position of row r's chunk c inside the LDS buffer.
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+    return c ^ ((((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1));
+}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     using Gm = PrefillGeom<T, D>;
     constexpr bool kBF = !__is_same(T, float);
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Gm::STAGE];
+    constexpr int NS = Gm::kStages;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * Gm::STAGE];
+    __shared__ int32_t lds_bid[kMaxPrefillPages];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int g = blockIdx.y;
-    const int bid = blockIdx.x;
+    // Workgroup id = tile * Hkv + kv head: workgroups are handed to the eight
+    // XCDs round-robin, so with Hkv a multiple of 8 every query tile of one kv
+    // head runs on one XCD and re-reads that head's K/V pages from its L2.
+    const int g = blockIdx.x % p.Hkv;
+    const int bid = blockIdx.x / p.Hkv;
     const int BQ = p.tile_tokens;
 
     // ---- which sequence owns this tile: largest s with qsl[s]/BQ + s <= bid
@@ -95,7 +155,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
     const int pos_min = r.L - n + tok0;           // position of the tile's first token
     const int pos_max = pos_min + ntok - 1;       // ... and of its last
-    if (pos_max < r.a) {
+    if (pos_max < r.a || pos_max / kPage - r.first_page >= kMaxPrefillPages) {
         // every row sees no key (only with metadata outside the contract): write zeros
         for (int rr = tid; rr < ntok * p.G; rr += blockDim.x) {
             const int tok = rr / p.G, hh = rr % p.G;
@@ -107,10 +167,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     }
     const int first_page = r.first_page;
     const int last_page = pos_max / kPage;
-    const int nstage = (last_page - first_page + 2) / 2;
-    const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
+    const int npages = last_page - first_page + 1;
+    const int nstage = (npages + 1) / 2;
 
-    // ---- rows of this wavefront: two 16-column tiles
+    // ---- rows of this wavefront: two 16-column tiles; query operands first, so
+    // that their loads complete before any staged K/V load
     int pos[2];
     bool rvalid[2];
     int64_t orow_idx[2];
@@ -129,60 +190,94 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
             qop[nt][i] = rvalid[nt] ? v : u32x4{0, 0, 0, 0};
         }
     }
-
-    const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
-    const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
-    const int64_t page_stride = (int64_t)p.Hkv * kPage * Gm::RB;
-    const int64_t head_off = (int64_t)g * kPage * Gm::RB;
-
-    auto load_stage = [&](int st, u32x4 (&reg)[Gm::LCH]) {
-        const int pa = first_page + 2 * st;
-        const int64_t ba = safe_block(bt, pa, p.num_blocks);
-        const int64_t bb = safe_block(bt, pa + 1 <= last_page ? pa + 1 : pa, p.num_blocks);
-#pragma unroll
-        for (int c = 0; c < Gm::LCH; ++c) {
-            const int ci = c * (kPrefillWaves * kWave) + tid;
-            const int buf = ci / (kPage * Gm::CPR);
-            const int within = ci - buf * (kPage * Gm::CPR);
-            const uint8_t* pool = (buf < 2) ? kpool : vpool;
-            const int64_t blk = (buf & 1) ? bb : ba;
-            reg[c] = ld16(pool + blk * page_stride + head_off + (int64_t)within * 16);
-        }
-    };
-    auto store_stage = [&](int slot, const u32x4 (&reg)[Gm::LCH]) {
-        uint8_t* base = lds + slot * Gm::STAGE;
-#pragma unroll
-        for (int c = 0; c < Gm::LCH; ++c) {
-            const int ci = c * (kPrefillWaves * kWave) + tid;
-            const int buf = ci / (kPage * Gm::CPR);
-            const int within = ci - buf * (kPage * Gm::CPR);
-            const int row = within / Gm::CPR, cc = within - (within / Gm::CPR) * Gm::CPR;
-            st16(base + buf * Gm::PAGE_LDS + row * Gm::RS + cc * 16, reg[c]);
-        }
-    };
-
-    f32x4 acc[2][Gm::NT];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int t = 0; t < Gm::NT; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
-
     {
-        u32x4 reg[Gm::LCH];
-        load_stage(0, reg);
-        store_stage(0, reg);
+        const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
+        for (int i = tid; i < npages; i += blockDim.x) {
+            const int32_t b = bt[first_page + i];
+            lds_bid[i] = (b >= 0 && b < p.num_blocks) ? b : 0;
+        }
     }
     __syncthreads();
 
-    for (int st = 0; st < nstage; ++st) {
-        const int pa = first_page + 2 * st;
-        const bool more = st + 1 < nstage;
-        u32x4 reg[Gm::LCH];
-        if (more) load_stage(st + 1, reg);
-        const uint8_t* sb = lds + (st & 1) * Gm::STAGE;
+    const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
+    const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
+    const int64_t page_stride = (int64_t)p.Hkv * Gm::PAGE;
+    const int64_t head_off = (int64_t)g * Gm::PAGE;
 
+    // Stage st: wave w loads blocks w, w + 4, ...; block b covers rows
+    // (b % (PAGE/1KiB)) * ROWS_PER_BLOCK.. of buffer b / (PAGE/1KiB).  The
+    // lane's byte offset inside the (page, head) is fixed; per stage only the
+    // two page bases change.
+    constexpr int BPP = Gm::PAGE / 1024;  // blocks per page
+    int src_off[Gm::LPT];
+#pragma unroll
+    for (int c = 0; c < Gm::LPT; ++c) {
+        const int blk = c * kPrefillWaves + wave;
+        const int row = (blk % BPP) * Gm::ROWS_PER_BLOCK + lane / Gm::CPR;
+        src_off[c] = row * Gm::RB + swz<Gm::CPR>(row, lane % Gm::CPR) * 16;
+    }
+    auto issue_stage = [&](int st) {
+        const int pa = first_page + 2 * st;
+        const int pb = (pa + 1 <= last_page) ? pa + 1 : pa;
+        const int64_t ba = __builtin_amdgcn_readfirstlane(lds_bid[pa - first_page]);
+        const int64_t bb = __builtin_amdgcn_readfirstlane(lds_bid[pb - first_page]);
+        const uint8_t* kA = kpool + ba * page_stride + head_off;
+        const uint8_t* kB = kpool + bb * page_stride + head_off;
+        const uint8_t* vA = vpool + ba * page_stride + head_off;
+        const uint8_t* vB = vpool + bb * page_stride + head_off;
+        uint8_t* base = lds + (st % NS) * Gm::STAGE;
+#pragma unroll
+        for (int c = 0; c < Gm::LPT; ++c) {
+            const int blk = c * kPrefillWaves + wave;
+            const int buf = blk / BPP;                 // 0 K a, 1 K b, 2 V a, 3 V b
+            const uint8_t* src = buf == 0 ? kA : buf == 1 ? kB : buf == 2 ? vA : vB;
+            load_to_lds16(src + src_off[c], base + blk * 1024);
+        }
+    };
+    // LDS address of (row, chunk) of buffer `buf` in stage slot `slot`
+    auto lds_at = [&](int slot, int buf, int row, int chunk) {
+        return lds + slot * Gm::STAGE + buf * Gm::PAGE + row * Gm::RB + swz<Gm::CPR>(row, chunk) * 16;
+    };
+
+    f32x4 acc[2][Gm::NT];
+    f32x4 lsum[2];  // column sums of P, accumulated on the matrix cores
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        lsum[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < Gm::NT; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float m_run[2] = {-INFINITY, -INFINITY};
+
+    // Per-lane LDS offsets inside a stage buffer, fixed for the whole loop.
+    int koff[Gm::KCH];  // K operand: row col, chunk 4i + grp
+#pragma unroll
+    for (int i = 0; i < Gm::KCH; ++i)
+        koff[i] = col * Gm::RB + swz<Gm::CPR>(col, 4 * i + grp) * 16;
+    int voff[Gm::NT];   // bf16 V^T: row 4grp + col/4, columns 16t + 4(col%4) .. +3
+    {
+        const int vrow = 4 * grp + (col >> 2);
+        const int vsub = (col & 3) * 8;
+#pragma unroll
+        for (int t = 0; t < Gm::NT; ++t)
+            voff[t] = vrow * Gm::RB + swz<Gm::CPR>(vrow, 2 * t + (vsub >> 4)) * 16 + (vsub & 15);
+    }
+
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < nstage) issue_stage(st);
+
+    // One stage.  `slot_tag` is a compile-time ring slot (interior stages, so
+    // every LDS address is a register plus an immediate) or -1 (slot from st).
+    // EDGE stages mask keys outside [kv_start, position] and zero the V rows
+    // of keys outside [kv_start, pos_max].  The running max is raised lazily:
+    // only when some column's tile max exceeds it by more than 8 (log2 units);
+    // column sums of P come from one extra MFMA against an all-ones operand.
+    auto compute = [&](auto edge_tag, auto slot_tag, int st) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        constexpr int SLOT = decltype(slot_tag)::value;
+        const uint8_t* sb = lds + (SLOT >= 0 ? SLOT : st % NS) * Gm::STAGE;
+        const int pa = first_page + 2 * st;
         // ---- S^T tiles: keys of page x as rows, this wavefront's rows as columns
         f32x4 sx[2][2];
 #pragma unroll
@@ -190,7 +285,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
             u32x4 kop[Gm::KCH];
 #pragma unroll
             for (int i = 0; i < Gm::KCH; ++i)
-                kop[i] = ld16(sb + x * Gm::PAGE_LDS + col * Gm::RS + i * 64 + grp * 16);
+                kop[i] = *reinterpret_cast<const u32x4*>(sb + x * Gm::PAGE + koff[i]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -208,98 +303,154 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
                 sx[nt][x] = sacc;
             }
         }
-        const bool edge = (pa * kPage < r.a) || (pa * kPage + 2 * kPage - 1 > pos_min);
         bool kval[8];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int key = (pa + x) * kPage + grp * 4 + t;
-                kval[x * 4 + t] = !edge || (key >= r.a && key <= pos_max);
-            }
-        u32x4 pb[2];
-        float pv[2][8];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            float sv[8];
+        if constexpr (EDGE) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int key = (pa + x) * kPage + grp * 4 + t;
-                    const bool ok = !edge || (key >= r.a && key <= pos[nt]);
-                    sv[x * 4 + t] = ok ? sx[nt][x][t] * p.scale_log2 : -INFINITY;
+                    kval[x * 4 + t] = key >= r.a && key <= pos_max;
                 }
-            float mt = sv[0];
+        }
+        float sv[2][8];
+        bool grow = false;
 #pragma unroll
-            for (int t = 1; t < 8; ++t) mt = fmaxf(mt, sv[t]);
-            mt = col_max(mt);
-            const float m_new = fmaxf(m_run[nt], mt);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run[nt] - m_use);
-            m_run[nt] = m_new;
-            float psum = 0.f;
+        for (int nt = 0; nt < 2; ++nt) {
+            float mt = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                pv[nt][t] = fast_exp2(sv[t] - m_use);
-                psum += pv[nt][t];
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    float v = sx[nt][x][t];
+                    if constexpr (EDGE) {
+                        const int key = (pa + x) * kPage + grp * 4 + t;
+                        v = (key >= r.a && key <= pos[nt]) ? v : -INFINITY;
+                    }
+                    sv[nt][x * 4 + t] = v;
+                    mt = fmaxf(mt, v);
+                }
+            grow |= mt * p.scale_log2 > m_run[nt] + 8.f;
+        }
+        if (__any(grow)) {
+            // exact column maxima, then rescale what was accumulated so far
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float mt = sv[nt][0];
+#pragma unroll
+                for (int t = 1; t < 8; ++t) mt = fmaxf(mt, sv[nt][t]);
+                mt = col_max(mt) * p.scale_log2;
+                const float m_new = fmaxf(m_run[nt], mt);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run[nt] - m_use);
+                m_run[nt] = m_new;
+                lsum[nt] *= alpha;
+#pragma unroll
+                for (int t = 0; t < Gm::NT; ++t) acc[nt][t] *= alpha;
             }
-            l_run[nt] = l_run[nt] * alpha + psum;
+        }
+        u32x4 pb[2];
+        float pv[2][8];
 #pragma unroll
-            for (int t = 0; t < Gm::NT; ++t) acc[nt][t] *= alpha;
+        for (int nt = 0; nt < 2; ++nt) {
+            const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                pv[nt][t] = fast_exp2(__builtin_fmaf(sv[nt][t], p.scale_log2, -m_use));
             if constexpr (kBF)
                 pb[nt] = u32x4{pack_bf16(pv[nt][0], pv[nt][1]), pack_bf16(pv[nt][2], pv[nt][3]),
                                pack_bf16(pv[nt][4], pv[nt][5]), pack_bf16(pv[nt][6], pv[nt][7])};
         }
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T, and the column sums of P
         if constexpr (kBF) {
-            const uint16_t* l16 = reinterpret_cast<const uint16_t*>(sb + 2 * Gm::PAGE_LDS);
+            const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) lsum[nt] = mfma_bf16(ones, pb[nt], lsum[nt]);
+            uint32_t keep[4];
+            if constexpr (EDGE) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    keep[q] = (kval[2 * q] ? 0x0000ffffu : 0u) | (kval[2 * q + 1] ? 0xffff0000u : 0u);
+            }
 #pragma unroll
             for (int t = 0; t < Gm::NT; ++t) {
-                const int d = t * 16 + col;
-                u32x4 a;
+                const uint2 lo = lds_read_tr16(sb + 2 * Gm::PAGE + voff[t]);
+                const uint2 hi = lds_read_tr16(sb + 3 * Gm::PAGE + voff[t]);
+                u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                if constexpr (EDGE) {
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int x = w >> 1;
-                    const int k0 = grp * 4 + (w & 1) * 2;
-                    const int base = (x * Gm::PAGE_LDS + k0 * Gm::RS) / 2 + d;
-                    uint32_t lo16 = l16[base];
-                    uint32_t hi16 = l16[base + Gm::RS / 2];
-                    if (edge) {
-                        lo16 = kval[2 * w] ? lo16 : 0u;
-                        hi16 = kval[2 * w + 1] ? hi16 : 0u;
-                    }
-                    a[w] = lo16 | (hi16 << 16);
+                    for (int q = 0; q < 4; ++q) a[q] &= keep[q];
                 }
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) acc[nt][t] = mfma_bf16(a, pb[nt], acc[nt][t]);
             }
         } else {
-            const float* lf = reinterpret_cast<const float*>(sb + 2 * Gm::PAGE_LDS);
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int key = grp * 4 + u;
-                    const bool ok = kval[x * 4 + u];
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        lsum[nt] = mfma_f32(1.f, pv[nt][x * 4 + u], lsum[nt]);
 #pragma unroll
                     for (int t = 0; t < Gm::NT; ++t) {
-                        float v = lf[(x * Gm::PAGE_LDS + key * Gm::RS) / 4 + t * 16 + col];
-                        v = ok ? v : 0.f;
+                        const int dcol = t * 16 + col;
+                        float v = *reinterpret_cast<const float*>(
+                            sb + (2 + x) * Gm::PAGE + key * Gm::RB +
+                            swz<Gm::CPR>(key, dcol >> 2) * 16 + (dcol & 3) * 4);
+                        if constexpr (EDGE) v = kval[x * 4 + u] ? v : 0.f;
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt)
                             acc[nt][t] = mfma_f32(v, pv[nt][x * 4 + u], acc[nt][t]);
                     }
                 }
         }
-        if (more) store_stage((st + 1) & 1, reg);
-        __syncthreads();
+    };
+
+    auto step = [&](auto edge_tag, auto slot_tag, int st) {
+        // stage st's own loads are done when at most the later issued stages
+        // (up to NS - 2 of them) are still in flight
+        const int later = min(NS - 2, nstage - 1 - st);
+        if constexpr (NS == 4) {
+            if (later >= 2) wait_vmcnt<2 * Gm::LPT>();
+            else if (later == 1) wait_vmcnt<Gm::LPT>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier_keep_loads_in_flight();  // all of stage st is in LDS; slot (st-1) is free
+        if (st + NS - 1 < nstage) issue_stage(st + NS - 1);
+        compute(edge_tag, slot_tag, st);
+    };
+    using Dyn = std::integral_constant<int, -1>;
+    // Stage 0 and everything past the interior run take the masked path; the
+    // interior stages (all keys in [kv_start, first position of the tile])
+    // run unrolled over the ring with compile-time slots.
+    const int full = (pos_min - first_page * kPage - 2 * kPage + 1) < 0
+                         ? 0 : (pos_min - first_page * kPage - 2 * kPage + 1) / (2 * kPage) + 1;
+    const int st_hi = min(nstage, full);
+    step(std::true_type{}, Dyn{}, 0);
+    int st = 1;
+    if constexpr (NS == 4) {
+        for (; st + 3 < st_hi; st += 4) {
+            step(std::false_type{}, std::integral_constant<int, 1>{}, st);
+            step(std::false_type{}, std::integral_constant<int, 2>{}, st + 1);
+            step(std::false_type{}, std::integral_constant<int, 3>{}, st + 2);
+            step(std::false_type{}, std::integral_constant<int, 0>{}, st + 3);
+        }
+    } else {
+        for (; st + 1 < st_hi; st += 2) {
+            step(std::false_type{}, std::integral_constant<int, 1>{}, st);
+            step(std::false_type{}, std::integral_constant<int, 0>{}, st + 1);
+        }
     }
+    for (; st < nstage; ++st) step(std::true_type{}, Dyn{}, st);
 
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const float l_tot = col_sum(l_run[nt]);
+        const float l_tot = lsum[nt][0];  // every row of the ones-product holds the column sum
         if (!rvalid[nt]) continue;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint8_t* orow = static_cast<uint8_t*>(p.out) + orow_idx[nt] * Gm::RB;
