@@ -124,7 +124,7 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
     if (max_seqlen_q > 1) {
         const long tiles = (total_q + pp.tile_tokens - 1) / pp.tile_tokens + num_seqs;
         hipLaunchKernelGGL((pkv::prefill_kernel<T, D>), dim3((unsigned)(tiles * pp.Hkv)),
-                           dim3(pkv::kPrefillWaves * 64), 0, stream, pp);
+                           dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
         if (int rc = hip_status("prefill launch")) return rc;
     }
     return PKV_OK;

@@ -10,16 +10,20 @@
 // an n-token chunk over L keys sits at position L - n + i ("How vllm-metal fits
 // into vLLM": chunked prefill shares each step with decodes).
 //
-// Work unit: one workgroup of four wavefronts per (sequence, kv head, tile of
-// query tokens).  The G query heads of the kv head are folded into the tile's
-// rows (row = token * G + head), so every staged K/V page serves all of them.
-// Each wavefront owns 32 rows (two 16-column MFMA tiles), keys being the MFMA
-// rows:  S^T = K q^T,  O^T += V^T P^T.
+// Work unit: one workgroup per (sequence, kv head, tile of query tokens).
+// The G query heads of the kv head are folded into the tile's rows
+// (row = token * G + head), so every staged K/V page serves all of them.
+// Keys are the MFMA rows:  S^T = K q^T,  O^T += V^T P^T.  Four row blocks of
+// 32 rows (two 16-column MFMA tiles) cover the tile's 128 rows.  For bfloat16
+// each row block has two wavefronts on the same SIMD that take alternate KV
+// stages (eight wavefronts per workgroup), so one wavefront's softmax runs
+// while the other's products occupy the matrix core; their partial results
+// are combined through LDS at the end with the usual log-sum-exp rescaling.
 //
 // Staging: pairs of KV pages (32 keys; K and V of two pages, 16 KiB for bf16
 // head_dim 128) go from HBM straight into a ring of kStages LDS buffers with
-// global->LDS loads, kStages - 1 pairs ahead of the pair being consumed, one
-// barrier per pair.  Inside a buffer each 16-byte chunk of a row sits at
+// global->LDS loads, issued several rounds ahead of the stages being consumed,
+// one workgroup barrier per round.  Inside a buffer each 16-byte chunk of a row sits at
 // chunk ^ f(row), so the 16 key rows read for one K operand fall in distinct
 // banks.  V^T operands come from the transposing LDS read (ds_read_b64_tr_b16),
 // which hands each lane 4 consecutive keys of one column.  The workgroup's
@@ -56,8 +60,8 @@ struct PrefillParams {
     float scale_log2;
 };
 
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRows = 32 * kPrefillWaves;
+constexpr int kPrefillRowBlocks = 4;                 // 32-row blocks per workgroup
+constexpr int kPrefillRows = 32 * kPrefillRowBlocks;
 constexpr int kMaxPrefillPages = 4096;  // block-table entries a workgroup stages (64K keys)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -95,19 +99,35 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wavefronts per 32-row block: two for bfloat16 (alternate stages), one for float32
+template <typename T>
+constexpr int kPrefillSplit = __is_same(T, float) ? 1 : 2;
+template <typename T>
+constexpr int kPrefillThreads = kPrefillRowBlocks * kPrefillSplit<T> * kWave;
+
 template <typename T, int D>
 struct PrefillGeom {
+    static constexpr bool kBF = !__is_same(T, float);
+    static constexpr int SPLIT = kPrefillSplit<T>;
+    static constexpr int NW = kPrefillRowBlocks * SPLIT;   // wavefronts per workgroup
+    static constexpr int kThreads = kPrefillThreads<T>;
     static constexpr int EB = Elem<T>::kBytes;
-    static constexpr int RB = D * EB;                    // bytes per K/V row
-    static constexpr int CPR = RB / 16;                  // 16-byte chunks per row
-    static constexpr int PAGE = kPage * RB;              // bytes of one (page, head)
-    static constexpr int BLOCKS = 4 * PAGE / 1024;       // 1 KiB load blocks per stage
-    static constexpr int LPT = BLOCKS / kPrefillWaves;   // load instructions per thread
+    static constexpr int RB = D * EB;                      // bytes per K/V row
+    static constexpr int CPR = RB / 16;                    // 16-byte chunks per row
+    static constexpr int PAGE = kPage * RB;                // bytes of one (page, head)
+    static constexpr int STAGE = 4 * PAGE;                 // K a, K b, V a, V b
+    static constexpr int BLOCKS = STAGE / 1024;            // 1 KiB load blocks per stage
+    static constexpr int LPT = BLOCKS / NW;                // load instructions per thread
     static constexpr int ROWS_PER_BLOCK = 1024 / RB;
-    static constexpr int STAGE = 4 * PAGE;               // K a, K b, V a, V b
-    static constexpr int kStages = (STAGE <= 16384) ? 4 : 2;
+    // ring slots (a multiple of SPLIT; the ring stays within 128 KiB)
+    static constexpr int kStages = (STAGE <= 16384) ? (kBF ? 8 : 4) : 2;
     static constexpr int NT = D / 16;
     static constexpr int KCH = RB / 64;
+    // floats per lane handed from the second wavefront of a row block to the first
+    static constexpr int XF = 2 * NT * 4 + 4;
+    static_assert(LPT >= 1 && kStages % SPLIT == 0, "stage geometry");
+    static_assert(SPLIT == 1 || kPrefillRowBlocks * kWave * XF * 4 <= kStages * STAGE,
+                  "exchange area fits in the ring");
 };
 
 // Chunk position of row r's chunk c inside the LDS buffer.
@@ -116,11 +136,33 @@ __device__ __forceinline__ int swz(int r, int c) {
     return c ^ ((((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1));
 }
 
+// Waits until at most `later` stages of this thread's global->LDS loads (LPT
+// instructions each) are still in flight; later <= MAXL.
+template <int LPT, int MAXL>
+__device__ __forceinline__ void wait_stages(int later) {
+    if constexpr (MAXL == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= MAXL) wait_vmcnt<MAXL * LPT>();
+        else wait_stages<LPT, MAXL - 1>(later);
+    }
+}
+
+template <int K, int U, typename F>
+__device__ __forceinline__ void unroll_rounds(F&& f) {
+    if constexpr (K < U) {
+        f(std::integral_constant<int, K>{});
+        unroll_rounds<K + 1, U>(f);
+    }
+}
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillParams p) {
     using Gm = PrefillGeom<T, D>;
-    constexpr bool kBF = !__is_same(T, float);
+    constexpr bool kBF = Gm::kBF;
     constexpr int NS = Gm::kStages;
+    constexpr int SPLIT = Gm::SPLIT;
+    constexpr int NW = Gm::NW;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * Gm::STAGE];
     __shared__ int32_t lds_bid[kMaxPrefillPages];
 
@@ -129,6 +171,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
+    const int rblk = wave % kPrefillRowBlocks;  // 32-row block of this wavefront
+    const int half = wave / kPrefillRowBlocks;  // stages st with st % SPLIT == half
     // Workgroup id = tile * Hkv + kv head: workgroups are handed to the eight
     // XCDs round-robin, so with Hkv a multiple of 8 every query tile of one kv
     // head runs on one XCD and re-reads that head's K/V pages from its L2.
@@ -178,7 +222,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     u32x4 qop[2][Gm::KCH];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const int row = wave * 32 + nt * 16 + col;
+        const int row = rblk * 32 + nt * 16 + col;
         const int tok = row / p.G, hh = row - (row / p.G) * p.G;
         rvalid[nt] = tok < ntok;
         pos[nt] = rvalid[nt] ? pos_min + tok : -1;
@@ -204,7 +248,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     const int64_t page_stride = (int64_t)p.Hkv * Gm::PAGE;
     const int64_t head_off = (int64_t)g * Gm::PAGE;
 
-    // Stage st: wave w loads blocks w, w + 4, ...; block b covers rows
+    // Stage st: wavefront w loads blocks w, w + NW, ...; block b covers rows
     // (b % (PAGE/1KiB)) * ROWS_PER_BLOCK.. of buffer b / (PAGE/1KiB).  The
     // lane's byte offset inside the (page, head) is fixed; per stage only the
     // two page bases change.
@@ -212,7 +256,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     int src_off[Gm::LPT];
 #pragma unroll
     for (int c = 0; c < Gm::LPT; ++c) {
-        const int blk = c * kPrefillWaves + wave;
+        const int blk = c * NW + wave;
         const int row = (blk % BPP) * Gm::ROWS_PER_BLOCK + lane / Gm::CPR;
         src_off[c] = row * Gm::RB + swz<Gm::CPR>(row, lane % Gm::CPR) * 16;
     }
@@ -228,15 +272,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
         uint8_t* base = lds + (st % NS) * Gm::STAGE;
 #pragma unroll
         for (int c = 0; c < Gm::LPT; ++c) {
-            const int blk = c * kPrefillWaves + wave;
+            const int blk = c * NW + wave;
             const int buf = blk / BPP;                 // 0 K a, 1 K b, 2 V a, 3 V b
             const uint8_t* src = buf == 0 ? kA : buf == 1 ? kB : buf == 2 ? vA : vB;
             load_to_lds16(src + src_off[c], base + blk * 1024);
         }
-    };
-    // LDS address of (row, chunk) of buffer `buf` in stage slot `slot`
-    auto lds_at = [&](int slot, int buf, int row, int chunk) {
-        return lds + slot * Gm::STAGE + buf * Gm::PAGE + row * Gm::RB + swz<Gm::CPR>(row, chunk) * 16;
     };
 
     f32x4 acc[2][Gm::NT];
@@ -249,34 +289,35 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     }
     float m_run[2] = {-INFINITY, -INFINITY};
 
-    // Per-lane LDS offsets inside a stage buffer, fixed for the whole loop.
+    // Per-lane LDS offsets inside the ring, fixed for the whole loop; they
+    // include this wavefront's slot within a round (stage st sits in slot
+    // st % NS = (round * SPLIT) % NS + half).
+    const int hoff = SPLIT > 1 ? half * Gm::STAGE : 0;
     int koff[Gm::KCH];  // K operand: row col, chunk 4i + grp
 #pragma unroll
     for (int i = 0; i < Gm::KCH; ++i)
-        koff[i] = col * Gm::RB + swz<Gm::CPR>(col, 4 * i + grp) * 16;
+        koff[i] = hoff + col * Gm::RB + swz<Gm::CPR>(col, 4 * i + grp) * 16;
     int voff[Gm::NT];   // bf16 V^T: row 4grp + col/4, columns 16t + 4(col%4) .. +3
     {
         const int vrow = 4 * grp + (col >> 2);
         const int vsub = (col & 3) * 8;
 #pragma unroll
         for (int t = 0; t < Gm::NT; ++t)
-            voff[t] = vrow * Gm::RB + swz<Gm::CPR>(vrow, 2 * t + (vsub >> 4)) * 16 + (vsub & 15);
+            voff[t] = hoff + vrow * Gm::RB + swz<Gm::CPR>(vrow, 2 * t + (vsub >> 4)) * 16 +
+                      (vsub & 15);
     }
 
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st)
-        if (st < nstage) issue_stage(st);
-
-    // One stage.  `slot_tag` is a compile-time ring slot (interior stages, so
-    // every LDS address is a register plus an immediate) or -1 (slot from st).
-    // EDGE stages mask keys outside [kv_start, position] and zero the V rows
-    // of keys outside [kv_start, pos_max].  The running max is raised lazily:
-    // only when some column's tile max exceeds it by more than 8 (log2 units);
-    // column sums of P come from one extra MFMA against an all-ones operand.
-    auto compute = [&](auto edge_tag, auto slot_tag, int st) {
+    // One stage.  `slot_tag` is the compile-time ring slot of the round
+    // (interior rounds, so every LDS address is a register plus an immediate)
+    // or -1 (slot `dyn_slot`).  EDGE stages mask keys outside
+    // [kv_start, position] and zero the V rows of keys outside
+    // [kv_start, pos_max].  The running max is raised lazily: only when some
+    // column's tile max exceeds it by more than 8 (log2 units); column sums of
+    // P come from one extra MFMA against an all-ones operand.
+    auto compute = [&](auto edge_tag, auto slot_tag, int dyn_slot, int st) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         constexpr int SLOT = decltype(slot_tag)::value;
-        const uint8_t* sb = lds + (SLOT >= 0 ? SLOT : st % NS) * Gm::STAGE;
+        const uint8_t* sb = lds + (SLOT >= 0 ? SLOT : dyn_slot) * Gm::STAGE;
         const int pa = first_page + 2 * st;
         // ---- S^T tiles: keys of page x as rows, this wavefront's rows as columns
         f32x4 sx[2][2];
@@ -398,7 +439,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
                     for (int t = 0; t < Gm::NT; ++t) {
                         const int dcol = t * 16 + col;
                         float v = *reinterpret_cast<const float*>(
-                            sb + (2 + x) * Gm::PAGE + key * Gm::RB +
+                            sb + hoff + (2 + x) * Gm::PAGE + key * Gm::RB +
                             swz<Gm::CPR>(key, dcol >> 2) * 16 + (dcol & 3) * 4);
                         if constexpr (EDGE) v = kval[x * 4 + u] ? v : 0.f;
 #pragma unroll
@@ -409,50 +450,89 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
         }
     };
 
-    auto step = [&](auto edge_tag, auto slot_tag, int st) {
-        // stage st's own loads are done when at most the later issued stages
-        // (up to NS - 2 of them) are still in flight
-        const int later = min(NS - 2, nstage - 1 - st);
-        if constexpr (NS == 4) {
-            if (later >= 2) wait_vmcnt<2 * Gm::LPT>();
-            else if (later == 1) wait_vmcnt<Gm::LPT>();
-            else wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
+    // Round rr: stages rr * SPLIT .. rr * SPLIT + SPLIT - 1, one per wavefront
+    // of a row block.  Before the barrier this thread's loads of those stages
+    // are complete; after it every wavefront is done with round rr - 1, whose
+    // slots take the stages NS - SPLIT ahead.
+    auto round = [&](auto edge_tag, auto slot_tag, int rr) {
+        const int last_needed = min(rr * SPLIT + SPLIT - 1, nstage - 1);
+        const int last_issued = min(rr * SPLIT + NS - SPLIT - 1, nstage - 1);
+        wait_stages<Gm::LPT, NS - 2 * SPLIT>(last_issued - last_needed);
+        barrier_keep_loads_in_flight();
+#pragma unroll
+        for (int j = 0; j < SPLIT; ++j) {
+            const int st = rr * SPLIT + NS - SPLIT + j;
+            if (st < nstage) issue_stage(st);
         }
-        barrier_keep_loads_in_flight();  // all of stage st is in LDS; slot (st-1) is free
-        if (st + NS - 1 < nstage) issue_stage(st + NS - 1);
-        compute(edge_tag, slot_tag, st);
+        const int st = rr * SPLIT + half;
+        if (st < nstage) compute(edge_tag, slot_tag, (rr * SPLIT) % NS, st);
     };
+
+#pragma unroll
+    for (int st = 0; st < NS - SPLIT; ++st)
+        if (st < nstage) issue_stage(st);
+
     using Dyn = std::integral_constant<int, -1>;
-    // Stage 0 and everything past the interior run take the masked path; the
-    // interior stages (all keys in [kv_start, first position of the tile])
-    // run unrolled over the ring with compile-time slots.
+    // Round 0 and every round past the interior take the masked path; interior
+    // rounds (all keys in [kv_start, first position of the tile]) run unrolled
+    // over the ring with compile-time slots.
+    constexpr int U = NS / SPLIT;  // rounds per pass over the ring
+    const int nround = (nstage + SPLIT - 1) / SPLIT;
     const int full = (pos_min - first_page * kPage - 2 * kPage + 1) < 0
                          ? 0 : (pos_min - first_page * kPage - 2 * kPage + 1) / (2 * kPage) + 1;
-    const int st_hi = min(nstage, full);
-    step(std::true_type{}, Dyn{}, 0);
-    int st = 1;
-    if constexpr (NS == 4) {
-        for (; st + 3 < st_hi; st += 4) {
-            step(std::false_type{}, std::integral_constant<int, 1>{}, st);
-            step(std::false_type{}, std::integral_constant<int, 2>{}, st + 1);
-            step(std::false_type{}, std::integral_constant<int, 3>{}, st + 2);
-            step(std::false_type{}, std::integral_constant<int, 0>{}, st + 3);
+    const int r_hi = min(nstage, full) / SPLIT;  // rounds [1, r_hi) are interior
+    round(std::true_type{}, Dyn{}, 0);
+    int rr = 1;
+    for (; rr + U - 1 < r_hi; rr += U) {
+        unroll_rounds<0, U>([&](auto k) {
+            constexpr int KK = decltype(k)::value;
+            round(std::false_type{}, std::integral_constant<int, (SPLIT * (1 + KK)) % NS>{},
+                  rr + KK);
+        });
+    }
+    for (; rr < nround; ++rr) round(std::true_type{}, Dyn{}, rr);
+
+    float l_tot[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) l_tot[nt] = lsum[nt][0];  // every row holds the column sum
+    if constexpr (SPLIT > 1) {
+        // the second wavefront of each row block hands (acc, sum, max) to the first
+        __syncthreads();  // all reads of the ring are done; no loads in flight
+        float* xch = reinterpret_cast<float*>(lds) + rblk * Gm::XF * kWave + lane;
+        if (half != 0) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+                for (int t = 0; t < Gm::NT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xch[((nt * Gm::NT + t) * 4 + i) * kWave] = acc[nt][t][i];
+                xch[(2 * Gm::NT * 4 + 2 * nt) * kWave] = l_tot[nt];
+                xch[(2 * Gm::NT * 4 + 2 * nt + 1) * kWave] = m_run[nt];
+            }
         }
-    } else {
-        for (; st + 1 < st_hi; st += 2) {
-            step(std::false_type{}, std::integral_constant<int, 1>{}, st);
-            step(std::false_type{}, std::integral_constant<int, 0>{}, st + 1);
+        __syncthreads();
+        if (half != 0) return;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float l1 = xch[(2 * Gm::NT * 4 + 2 * nt) * kWave];
+            const float m1 = xch[(2 * Gm::NT * 4 + 2 * nt + 1) * kWave];
+            const float M = fmaxf(m_run[nt], m1);
+            const float Mu = (M == -INFINITY) ? 0.f : M;
+            const float a0 = fast_exp2(m_run[nt] - Mu);
+            const float a1 = fast_exp2(m1 - Mu);
+            l_tot[nt] = a0 * l_tot[nt] + a1 * l1;
+#pragma unroll
+            for (int t = 0; t < Gm::NT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[nt][t][i] = a0 * acc[nt][t][i] + a1 * xch[((nt * Gm::NT + t) * 4 + i) * kWave];
         }
     }
-    for (; st < nstage; ++st) step(std::true_type{}, Dyn{}, st);
 
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const float l_tot = lsum[nt][0];  // every row of the ones-product holds the column sum
         if (!rvalid[nt]) continue;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv = l_tot[nt] > 0.f ? 1.f / l_tot[nt] : 0.f;
         uint8_t* orow = static_cast<uint8_t*>(p.out) + orow_idx[nt] * Gm::RB;
 #pragma unroll
         for (int t = 0; t < Gm::NT; ++t) {
