@@ -15,7 +15,9 @@ back steps read HBM.  One JSON line is printed:
              8 TB/s HBM peak, timed with HIP events on the launch stream
   cpu_baseline  the float64 oracle on the host cores over a bounded sample
   extra      the mixed chunked-prefill step: packed-step tokens/s and the
-             prefill kernel's MFMA utilisation against 2.5 PFLOP/s dense bf16
+             prefill kernel's MFMA utilisation against 2.5 PFLOP/s dense bf16;
+             a step of 4-token speculative-verify windows against the plain
+             decode step over the same contexts
 """
 from __future__ import annotations
 
@@ -249,6 +251,28 @@ def extra_prefill(steps: int, warmup: int):
     return res
 
 
+def extra_windows(steps: int, warmup: int):
+    """Speculative-verify windows on the 16-sequence decode shape (contexts
+    uniform in [1024, 4096], 16 query / 8 kv heads): every sequence verifies a
+    4-token window (3 draft tokens) through the decode path, timed against the
+    plain one-token decode step over the same contexts; caches cleared before
+    every step."""
+    lens = np.random.default_rng(2000).integers(1024, 4096, size=16, endpoint=True).tolist()
+    res = {"workload": "verify-window-16seq", "window_tokens": 4}
+    for name, n in (("window", 4), ("decode", 1)):
+        st = W.build_step(f"{name}-16seq", lens, [n] * 16, 16, 8, 128, torch.bfloat16, 2100,
+                          poison=False)
+        sm = Step(st, gen_device="cuda")
+        wall, attn, _, _ = time_steps(sm, steps, warmup, flush_bytes=1 << 30)
+        res[f"{name}_step_ms"] = wall * 1e3
+        res[f"{name}_attention_ms"] = attn * 1e3
+        res[f"{name}_tokens_per_s"] = st.total_q / wall
+        res[f"{name}_kv_gbs"] = kv_bytes(st) / wall / 1e9
+        del sm
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,7 +328,7 @@ def bench_single(k, args):
         "device_copy_gbs": copy_gbs,
         "copy_frac": gbs / copy_gbs,
         "packed_step_tokens_per_s": st.total_q / wall,
-        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_plan_kernel + decode_kernel + merge_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"decode_{st.name}"),
@@ -315,6 +339,7 @@ def bench_single(k, args):
     torch.cuda.empty_cache()
     if not args.no_extra and k != 3:
         rec["extra"] = extra_prefill(min(args.steps, 20), args.warmup)
+        rec["extra"]["verify_windows"] = extra_windows(min(args.steps, 20), args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(st)
     return rec
@@ -371,7 +396,7 @@ def bench_agent(k, args):
                    "page_size": 16, "logical_kv_bytes_per_step": logical,
                    "unique_kv_bytes_per_step": unique},
         "packed_step_tokens_per_s": b.num_seqs / wall,
-        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_plan_kernel + decode_kernel + merge_kernel)",
                      "achieved": unique / attn / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": unique / attn / 1e9 / HBM_PEAK_GBS, "traffic": None,
                      "launch_ms_mean": attn * 1e3, "algorithmic_bytes_per_launch": unique},

@@ -92,7 +92,8 @@ int pkv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool,
  * pkv_attention_workspace_size -- bytes of device workspace pkv_attention needs
  * for a step with these host bounds (host-only, pure; 0 if none is needed).
  * The same arguments must be passed to pkv_attention.  The workspace holds the
- * float32 partial results of the split-key decode pass.
+ * float32 partial results of the split-key decode pass (their size grows with
+ * the decode window W, see pkv_attention).
  */
 size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqlen_q,
                                     int max_seqlen_k, int num_q_heads, int num_kv_heads,
@@ -114,13 +115,18 @@ size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqle
  *
  * Host bounds: max_seqlen_q >= every sequence's query count, max_seqlen_k >=
  * every seq_lens[s]; both size the launch grids.  total_q = query_start_loc
- * [num_seqs].  Sequences with one query token take the split-key decode path;
- * sequences with two or more take the chunked-prefill path.  A sequence with
- * zero query tokens contributes nothing.
+ * [num_seqs].  With G = num_q_heads / num_kv_heads and
+ * W = min(16 / G, max_seqlen_q) (integer division), sequences with 1..W query
+ * tokens -- decodes, and speculative-verify windows of a few draft tokens --
+ * take the split-key decode path; sequences with more take the chunked-prefill
+ * path (vllm-metal v0.4.0 release post, "How vllm-metal fits into vLLM": one
+ * packed step holds prefill chunks, decode tokens and verify windows).  Both
+ * apply the same causal rule.  A sequence with zero query tokens contributes
+ * nothing.
  *
  * Supported: dtype F32/BF16 (q, pools and out share it), head_dim 64 or 128,
  * block_size 16, num_q_heads % num_kv_heads == 0 and 1 <= group size <= 16,
- * num_seqs <= 16384, and max_seqlen_k <= 65536 when max_seqlen_q > 1 (a
+ * num_seqs <= 16384, and max_seqlen_k <= 65536 when max_seqlen_q > W (a
  * prefill workgroup stages its block-table entries on chip); otherwise
  * PKV_E_UNSUPPORTED.
  * out must not alias q or the pools.  workspace must hold at least

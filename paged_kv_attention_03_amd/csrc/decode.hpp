@@ -1,5 +1,6 @@
-// Split-key decode attention for sequences with one query token, and the
-// merge of the per-split partial results.
+// Split-key decode attention for sequences with a few query tokens (one for a
+// plain decode, k + 1 for a speculative-verify window of k draft tokens), and
+// the merge of the per-split partial results.
 //
 // A decode step reads every visible key and value once and does a few flops
 // per byte: it is bound by memory bandwidth (vllm-metal v0.4.0 release post,
@@ -18,9 +19,10 @@
 // per wave, which a small merge kernel combines with the usual log-sum-exp
 // rescaling.
 //
-// Per page pair, the G query heads that share kv head g are the 16 columns of
-// a 16x16 matrix-core tile (columns >= G are zero), so one pass over a page
-// serves all of them:
+// Per page pair, the query rows that share kv head g -- the G heads of each of
+// the sequence's n query tokens, column = token * G + head, G * n <= 16 -- are
+// the 16 columns of a 16x16 matrix-core tile (unused columns are zero), so one
+// pass over a page serves all of them:
 //   S^T[key][head] = K_page[key][:] . q[head][:]      (MFMA, keys as rows)
 //   O^T[d][head]  += V^T[d][key] * P^T[key][head]      (MFMA, d as rows)
 // K goes straight from global memory into the A-operand registers (each lane
@@ -31,7 +33,11 @@
 // column is a two-step wavefront shuffle.  Keys outside [kv_start, seq_len)
 // are masked by selection, and their V entries are zeroed before the product,
 // so whatever bytes a partial or padding page holds (NaN included) never
-// reaches the output.
+// reaches the output.  Inside a window, token i of n sits at position
+// seq_len - n + i and sees keys up to its own position: a per-column cap that
+// only the last page pair of a segment can reach ("How vllm-metal fits into
+// vLLM": a packed step mixes prefill chunks, decode tokens and speculative
+// verify windows).
 #pragma once
 
 #include <type_traits>
@@ -50,8 +56,9 @@ struct Portion {
     int32_t s, g, pi0, pi1;
     int32_t slot;          // -1: the whole segment is here, write the output;
                            // else partial slot (wave * 2 + 0 first / 1 last piece)
-    int32_t q0;            // query row of the sequence
-    int32_t kv_lo, kv_hi;  // visible keys [kv_lo, kv_hi)
+    int32_t q0;            // first query row of the sequence
+    int32_t kv_lo, kv_hi;  // keys [kv_lo, kv_hi); token i of nq sees up to kv_hi - nq + i
+    int32_t nq;            // query tokens of the sequence (1 <= nq <= wmax)
 };
 
 struct PlanParams {
@@ -62,6 +69,7 @@ struct PlanParams {
     int Hkv;
     int max_seqlen_k;
     int max_blocks;
+    int wmax;                // sequences with 1..wmax query tokens take this path
     int64_t total_q;
     int32_t* pair_prefix;    // [num_seqs + 1] page pairs of sequences before s
     int32_t* portion_begin;  // [kDecodeWaves + 1]
@@ -76,12 +84,14 @@ struct DecodeParams {
     const int32_t* block_tables;
     const int32_t* portion_begin;
     const Portion* portions;
-    float* ws_o;    // [kDecodeWaves * 2][G][D] unnormalised partial outputs
-    float* ws_ml;   // [kDecodeWaves * 2][G][2] (running max in log2 units, sum)
+    float* ws_o;    // [kDecodeWaves * 2][ncol][D] unnormalised partial outputs
+    float* ws_ml;   // [kDecodeWaves * 2][ncol][2] (running max in log2 units, sum)
     int max_blocks;
     int Hq;
     int Hkv;
     int G;
+    int gmagic;     // ceil(2^16 / G): col / G == (col * gmagic) >> 16 for col < 16
+    int ncol;       // G * wmax columns per partial slot
     int64_t num_blocks;
     float scale_log2;  // softmax scale * log2(e)
 };
@@ -96,6 +106,7 @@ struct MergeParams {
     int Hq;
     int Hkv;
     int G;
+    int ncol;
 };
 
 // Start of wave w's unit range, and the wave whose range holds unit u.
@@ -146,7 +157,8 @@ __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(PlanParams p)
     const int S = p.num_seqs;
     for (int s = t; s < S; s += kPlanThreads) {
         const int q0 = p.qsl[s];
-        const bool dec = (p.qsl[s + 1] - q0 == 1) && q0 >= 0 && q0 < p.total_q;
+        const int nq = p.qsl[s + 1] - q0;
+        const bool dec = nq >= 1 && nq <= p.wmax && q0 >= 0 && q0 <= p.total_q - nq;
         const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
         C[s] = dec ? (r.end_page - r.first_page + 1) / 2 : 0;
     }
@@ -178,6 +190,7 @@ __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(PlanParams p)
                 q.pi1 = (int32_t)(min(u1, seg1) - seg0);
                 q.slot = (seg0 >= u0 && seg1 <= u1) ? -1 : w * 2 + (count == 0 ? 0 : 1);
                 q.q0 = p.qsl[s];
+                q.nq = p.qsl[s + 1] - q.q0;
                 const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
                 q.kv_lo = r.a;
                 q.kv_hi = r.L;
@@ -228,6 +241,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     constexpr bool kBF = !__is_same(T, float);
     __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * Gm::PAGE_LDS];
     __shared__ int32_t lds_bid[kWindowPages];
+    __shared__ Portion lds_port[kWave];  // this batch's segment pieces
 
     const int lane = threadIdx.x;
     const int col = lane & 15;
@@ -240,24 +254,39 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
     const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
     const int64_t page_stride = (int64_t)p.Hkv * kPage * Gm::RB;  // bytes per physical page
-    const bool hvalid = col < p.G;
+    // This lane's column is query token col / G, head col % G of the kv head's
+    // group.  The quotient is recomputed where it is needed (a multiply by
+    // ceil(2^16 / G) and a shift, exact for col < 16) rather than held in a
+    // register across the streaming loop; the empty asm keeps the compiler from
+    // hoisting it there.
+    auto col_tok = [&]() {
+        int m = p.gmagic;
+        asm volatile("" : "+s"(m));
+        return (col * m) >> 16;
+    };
 
     for (int b0 = pb; b0 < pe; b0 += kWave) {
         // ---- this batch's segment pieces, one per lane
         const int n = min(kWave, pe - b0);
-        Portion mine = {};
-        if (lane < n) mine = p.portions[b0 + lane];
-        int npairs = lane < n ? mine.pi1 - mine.pi0 : 0;
+        int npairs = 0;
+        wave_lds_fence();  // the previous batch is done with lds_port
+        if (lane < n) {
+            const Portion q = p.portions[b0 + lane];
+            lds_port[lane] = q;
+            npairs = q.pi1 - q.pi0;
+        }
+        wave_lds_fence();
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) npairs += __shfl_xor(npairs, off);
         const int K = npairs;
-        auto field = [&](int32_t v, int idx) { return __builtin_amdgcn_readlane(v, idx); };
+        // a field of piece idx (uniform), read back from LDS into a scalar register
+#define PKV_FIELD(name, idx) __builtin_amdgcn_readfirstlane(lds_port[idx].name)
 
         // ---- issue cursor (runs two pairs ahead of the process cursor)
-        int ip = 0, ipi = field(mine.pi0, 0), iend = field(mine.pi1, 0);
-        int is = field(mine.s, 0), ig = field(mine.g, 0);
-        int ifirst = field(mine.kv_lo, 0) / kPage;
-        int iendpg = (field(mine.kv_hi, 0) + kPage - 1) / kPage;
+        int ip = 0, ipi = PKV_FIELD(pi0, 0), iend = PKV_FIELD(pi1, 0);
+        int is = PKV_FIELD(s, 0), ig = PKV_FIELD(g, 0);
+        int ifirst = PKV_FIELD(kv_lo, 0) / kPage;
+        int iendpg = (PKV_FIELD(kv_hi, 0) + kPage - 1) / kPage;
         int wstart = -1, wseq = -1;
         bool idone = false;
 
@@ -299,12 +328,12 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
             if (!idone && ++ipi == iend) {
                 if (ip + 1 < n) {
                     ++ip;
-                    ipi = field(mine.pi0, ip);
-                    iend = field(mine.pi1, ip);
-                    is = field(mine.s, ip);
-                    ig = field(mine.g, ip);
-                    ifirst = field(mine.kv_lo, ip) / kPage;
-                    iendpg = (field(mine.kv_hi, ip) + kPage - 1) / kPage;
+                    ipi = PKV_FIELD(pi0, ip);
+                    iend = PKV_FIELD(pi1, ip);
+                    is = PKV_FIELD(s, ip);
+                    ig = PKV_FIELD(g, ip);
+                    ifirst = PKV_FIELD(kv_lo, ip) / kPage;
+                    iendpg = (PKV_FIELD(kv_hi, ip) + kPage - 1) / kPage;
                 } else {
                     idone = true;
                     --ipi;
@@ -315,24 +344,32 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
         // ---- process cursor state: the segment piece being accumulated
         int pp = -1, ppi = 0, pend = 0;
         int ps = 0, pg_ = 0, pslot = 0, pq0 = 0, plo = 0, phi = 0, pfirst = 0;
+        int plast = 0;   // last key the window's first token sees: seq_len - nq
+        int pnq = 1;
+        int pinner = 0;  // pairs [0, pinner) of the segment end at or before plast
         u32x4 qop[Gm::KCH];
         f32x4 acc[Gm::NT];
         float m_run = -INFINITY, l_run = 0.f;
 
         auto begin_piece = [&](int idx) {
             pp = idx;
-            ppi = field(mine.pi0, idx);
-            pend = field(mine.pi1, idx);
-            ps = field(mine.s, idx);
-            pg_ = field(mine.g, idx);
-            pslot = field(mine.slot, idx);
-            pq0 = field(mine.q0, idx);
-            plo = field(mine.kv_lo, idx);
-            phi = field(mine.kv_hi, idx);
+            ppi = PKV_FIELD(pi0, idx);
+            pend = PKV_FIELD(pi1, idx);
+            ps = PKV_FIELD(s, idx);
+            pg_ = PKV_FIELD(g, idx);
+            pslot = PKV_FIELD(slot, idx);
+            pq0 = PKV_FIELD(q0, idx);
+            plo = PKV_FIELD(kv_lo, idx);
+            phi = PKV_FIELD(kv_hi, idx);
+            pnq = PKV_FIELD(nq, idx);
+            plast = phi - pnq;
             pfirst = plo / kPage;
-            const int h = pg_ * p.G + col;
+            pinner = max(0, (plast + 1 - pfirst * kPage) / (2 * kPage));
+            const int ctok = col_tok();
+            const bool hvalid = ctok < pnq;
             const uint8_t* qrow = static_cast<const uint8_t*>(p.q) +
-                                  ((int64_t)pq0 * p.Hq + (hvalid ? h : 0)) * Gm::RB;
+                                  (hvalid ? ((int64_t)(pq0 + ctok) * p.Hq + pg_ * p.G + col - ctok * p.G) : 0) *
+                                      Gm::RB;
 #pragma unroll
             for (int i = 0; i < Gm::KCH; ++i) {
                 u32x4 v = ld16(qrow + i * 64 + grp * 16);
@@ -346,11 +383,12 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
 
         auto finish_piece = [&]() {
             const float l_tot = col_sum(l_run);
-            if (!hvalid) return;
-            const int h = pg_ * p.G + col;
+            const int ctok = col_tok();
+            if (ctok >= pnq) return;
             if (pslot < 0) {
                 const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-                uint8_t* orow = static_cast<uint8_t*>(p.out) + ((int64_t)pq0 * p.Hq + h) * Gm::RB;
+                uint8_t* orow = static_cast<uint8_t*>(p.out) +
+                                ((int64_t)(pq0 + ctok) * p.Hq + pg_ * p.G + col - ctok * p.G) * Gm::RB;
 #pragma unroll
                 for (int t = 0; t < Gm::NT; ++t) {
                     const int d = t * 16 + grp * 4;
@@ -363,7 +401,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                     }
                 }
             } else {
-                const int64_t slot = (int64_t)pslot * p.G + col;
+                const int64_t slot = (int64_t)pslot * p.ncol + col;
                 float* o = p.ws_o + slot * D;
 #pragma unroll
                 for (int t = 0; t < Gm::NT; ++t)
@@ -375,14 +413,16 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
             }
         };
 
-        // One pair of pages.  `edge` pairs (partly outside [kv_lo, kv_hi)) mask
-        // keys and zero their V entries; interior pairs skip all masking.  The
-        // running max is raised lazily: only when a tile's max exceeds it by
-        // more than 8 (log2 units), so probabilities stay below 2^8 and the
-        // accumulator rescale is rare.
+        // One pair of pages.  `edge` pairs (partly outside [kv_lo, kv_hi), or
+        // reaching past the first window token's position) mask keys and zero
+        // the V entries of keys outside [kv_lo, kv_hi); interior pairs skip all
+        // masking.  The running max is raised lazily: only when a tile's max
+        // exceeds it by more than 8 (log2 units), so probabilities stay below
+        // 2^8 and the accumulator rescale is rare.
         auto process = [&](auto edge_tag, int pa, const PairRegs<T, D>& R) {
             constexpr bool EDGE = decltype(edge_tag)::value;
             const int kv_lo = plo, kv_hi = phi;
+            const int cap = plast + (EDGE ? col_tok() : 0);  // last key this column's token sees
             // stage V (row-major, padded rows) for the transposed reads below
 #pragma unroll
             for (int x = 0; x < 2; ++x)
@@ -412,16 +452,21 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                 }
                 sx[x] = sacc;
             }
+            // key (x, t) of this lane: (pa + x) * kPage + 4 * grp + t; stored keys
+            // lie in [kv_lo, kv_hi) (V entries of the rest are zeroed below) and
+            // this column's token sees the stored keys up to cap
+            auto stored = [&](int x, int t) {
+                const int key = (pa + x) * kPage + grp * 4 + t;
+                return (unsigned)(key - kv_lo) < (unsigned)(kv_hi - kv_lo);
+            };
             float sv[8];
-            bool valid[8];
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int key = (pa + x) * kPage + grp * 4 + t;
-                    valid[x * 4 + t] =
-                        !EDGE || (unsigned)(key - kv_lo) < (unsigned)(kv_hi - kv_lo);
-                    sv[x * 4 + t] = valid[x * 4 + t] ? sx[x][t] * p.scale_log2 : -INFINITY;
+                    const bool seen = !EDGE || (key >= kv_lo && key <= min(cap, kv_hi - 1));
+                    sv[x * 4 + t] = seen ? sx[x][t] * p.scale_log2 : -INFINITY;
                 }
             float mt = sv[0];
 #pragma unroll
@@ -452,10 +497,14 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                              pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
                 const uint16_t* l16 = reinterpret_cast<const uint16_t*>(lds_v);
                 uint32_t keep[4];
+                if constexpr (EDGE) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    keep[q] = (valid[2 * q] ? 0x0000ffffu : 0u) |
-                              (valid[2 * q + 1] ? 0xffff0000u : 0u);
+                    for (int q = 0; q < 4; ++q) {
+                        const int x = q >> 1, t = (q & 1) * 2;
+                        keep[q] = (stored(x, t) ? 0x0000ffffu : 0u) |
+                                  (stored(x, t + 1) ? 0xffff0000u : 0u);
+                    }
+                }
 #pragma unroll
                 for (int t = 0; t < Gm::NT; ++t) {
                     const int d = t * 16 + col;
@@ -480,7 +529,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
 #pragma unroll
                         for (int t = 0; t < Gm::NT; ++t) {
                             float v = lf[(x * Gm::PAGE_LDS + key * Gm::RS) / 4 + t * 16 + col];
-                            if constexpr (EDGE) v = valid[x * 4 + u] ? v : 0.f;
+                            if constexpr (EDGE) v = stored(x, u) ? v : 0.f;
                             acc[t] = mfma_f32(v, pv[x * 4 + u], acc[t]);
                         }
                     }
@@ -494,7 +543,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                 begin_piece(pp + 1);
             }
             const int pa = pfirst + 2 * ppi;
-            if ((pa * kPage < plo) || ((pa + 2) * kPage > phi))
+            if ((ppi == 0 && plo != pfirst * kPage) || ppi >= pinner)
                 process(std::true_type{}, pa, R);
             else
                 process(std::false_type{}, pa, R);
@@ -516,64 +565,98 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     }
 }
 
+#undef PKV_FIELD
+
 // One wavefront per (sequence, query head) whose segment was cut by a wave
-// boundary: out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over its
-// pieces, rounded to the output type.
+// boundary, for each of the sequence's query tokens:
+// out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over its pieces,
+// rounded to the output type.  Lane j takes the j-th decode wave of
+// the segment (waves whose unit range is empty hold nothing: they lie between
+// the segment's waves when there are fewer units than waves); maxima and sums
+// combine across lanes, then every lane sums its output elements over the
+// pieces with eight loads in flight at a time.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) merge_kernel(MergeParams p) {
     constexpr bool kBF = !__is_same(T, float);
+    constexpr int PER = D / kWave;  // output elements per lane (1 or 2)
     const int h = blockIdx.x % p.Hq;
     const int s = blockIdx.x / p.Hq;
     if (s >= p.num_seqs) return;
     const int64_t c = p.pair_prefix[s + 1] - p.pair_prefix[s];
     if (c <= 0) return;
     const int64_t U = (int64_t)p.Hkv * p.pair_prefix[p.num_seqs];
-    const int g = h / p.G, col = h - (h / p.G) * p.G;
+    const int g = h / p.G, head = h - (h / p.G) * p.G;
     const int64_t a = (int64_t)p.Hkv * p.pair_prefix[s] + g * c;
     const int64_t wa = wave_of(a, U), wb = wave_of(a + c - 1, U);
     if (wa == wb) return;  // the wave that holds the whole segment wrote it
-    auto slot_of = [&](int64_t w) {
+    const int lane = threadIdx.x;
+    const int q0 = p.qsl[s];
+    const int nq = p.qsl[s + 1] - q0;
+    auto holds = [&](int64_t w) { return w <= wb && wave_start(w, U) < wave_start(w + 1, U); };
+    // first-piece slot of wave w, or its second piece when w's range starts before a
+    auto slot_row = [&](int64_t w) -> int32_t {
         const int which = (w == wa && wave_start(wa, U) != a) ? 1 : 0;
-        return (w * 2 + which) * p.G + col;
+        return (int32_t)((w * 2 + which) * p.ncol);
     };
-    // The waves holding the segment's units, each visited once: when there are
-    // fewer units than waves, waves with empty ranges lie between them.
-    const int64_t seg_end = a + c;
-    float M = -INFINITY;
-    for (int64_t u = a; u < seg_end;) {
-        const int64_t w = wave_of(u, U);
-        M = fmaxf(M, p.ws_ml[slot_of(w) * 2]);
-        u = wave_start(w + 1, U);
-    }
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    constexpr int PER = D / kWave;  // output elements per lane (1 or 2)
-    float num[PER], den = 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = 0.f;
-    for (int64_t u = a; u < seg_end;) {
-        const int64_t w = wave_of(u, U);
-        u = wave_start(w + 1, U);
-        const int64_t sl = slot_of(w);
-        const float wt = fast_exp2(p.ws_ml[sl * 2] - Mu);
-        den += wt * p.ws_ml[sl * 2 + 1];
-        const float* o = p.ws_o + sl * D;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += wt * o[threadIdx.x * PER + e];
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint8_t* orow = static_cast<uint8_t*>(p.out) +
-                    ((int64_t)p.qsl[s] * p.Hq + h) * (int64_t)D * Elem<T>::kBytes;
-    if constexpr (kBF) {
-        if constexpr (PER == 2) {
-            reinterpret_cast<uint32_t*>(orow)[threadIdx.x] = pack_bf16(num[0] * inv, num[1] * inv);
-        } else {
-            reinterpret_cast<uint16_t*>(orow)[threadIdx.x] =
-                (uint16_t)(pack_bf16(num[0] * inv, 0.f) & 0xffffu);
+
+    for (int tok = 0; tok < nq; ++tok) {
+        const int column = tok * p.G + head;
+        float M = -INFINITY;
+        for (int64_t w0 = wa; w0 <= wb; w0 += kWave) {
+            const int64_t w = w0 + lane;
+            if (holds(w)) M = fmaxf(M, p.ws_ml[(int64_t)(slot_row(w) + column) * 2]);
         }
-    } else {
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            reinterpret_cast<float*>(orow)[threadIdx.x * PER + e] = num[e] * inv;
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+
+        float num[PER], den = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] = 0.f;
+        for (int64_t w0 = wa; w0 <= wb; w0 += kWave) {
+            const int64_t w = w0 + lane;
+            const bool mine = holds(w);
+            const int32_t sl = (mine ? slot_row(w) : slot_row(wa)) + column;
+            const float wt = mine ? fast_exp2(p.ws_ml[(int64_t)sl * 2] - Mu) : 0.f;
+            if (mine) den += wt * p.ws_ml[(int64_t)sl * 2 + 1];
+            const int nb = (int)min((int64_t)kWave, wb - w0 + 1);
+            for (int j0 = 0; j0 < nb; j0 += 8) {
+                float o[8][PER];
+                bool use[8];
+                float wj[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int j = min(j0 + k, nb - 1);
+                    const int32_t slj = __builtin_amdgcn_readlane(sl, j);
+                    wj[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
+                    use[k] = (j0 + k < nb) && __builtin_amdgcn_readlane((int)mine, j) != 0;
+                    const float* src = p.ws_o + (int64_t)slj * D + lane * PER;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) o[k][e] = src[e];
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) num[e] += use[k] ? wj[k] * o[k][e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        uint8_t* orow = static_cast<uint8_t*>(p.out) +
+                        ((int64_t)(q0 + tok) * p.Hq + h) * (int64_t)D * Elem<T>::kBytes;
+        if constexpr (kBF) {
+            if constexpr (PER == 2) {
+                reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16(num[0] * inv, num[1] * inv);
+            } else {
+                reinterpret_cast<uint16_t*>(orow)[lane] =
+                    (uint16_t)(pack_bf16(num[0] * inv, 0.f) & 0xffffu);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                reinterpret_cast<float*>(orow)[lane * PER + e] = num[e] * inv;
+        }
     }
 }
 

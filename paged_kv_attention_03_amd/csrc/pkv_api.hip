@@ -62,19 +62,30 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 //   pair_prefix   int32[num_seqs + 1]          page pairs of decode sequences before s
 //   portion_begin int32[kDecodeWaves + 1]      each wave's first segment piece
 //   portions      Portion[kDecodeWaves + num_seqs * Hkv]
-//   ws_o          float[kDecodeWaves * 2][G][D] partial outputs of cut segments
-//   ws_ml         float[kDecodeWaves * 2][G][2] their running max and sum
+//   ws_o          float[kDecodeWaves * 2][ncol][D] partial outputs of cut segments
+//   ws_ml         float[kDecodeWaves * 2][ncol][2] their running max and sum
+// ncol = G * wmax: the query rows of one kv head in a sequence of the decode
+// path (up to wmax = min(16 / G, max_seqlen_q) query tokens).
 struct Plan {
     size_t off_prefix = 0, off_pbegin = 0, off_portions = 0, off_o = 0, off_ml = 0, total = 0;
     int prefill_tile_tokens = 0;
+    int wmax = 1;  // sequences with 1..wmax query tokens take the decode path
 };
 
 constexpr int kBlock = 16;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Plan make_plan(int num_seqs, int num_kv_heads, int head_dim, int group) {
+// Query tokens a sequence of the decode path may have: its G * n query rows
+// must fit the 16 columns of one matrix-core tile.
+int decode_window(int group, int max_seqlen_q) {
+    return std::max(1, std::min(16 / group, max_seqlen_q));
+}
+
+Plan make_plan(int num_seqs, int num_kv_heads, int head_dim, int group, int max_seqlen_q) {
     Plan pl;
+    pl.wmax = decode_window(group, max_seqlen_q);
+    const size_t ncol = (size_t)group * pl.wmax;
     size_t off = 0;
     pl.off_prefix = off;
     off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
@@ -83,9 +94,9 @@ Plan make_plan(int num_seqs, int num_kv_heads, int head_dim, int group) {
     pl.off_portions = off;
     off = align256(off + sizeof(pkv::Portion) * ((size_t)pkv::kDecodeWaves + (size_t)num_seqs * num_kv_heads));
     pl.off_o = off;
-    off = align256(off + sizeof(float) * (size_t)pkv::kDecodeWaves * 2 * group * head_dim);
+    off = align256(off + sizeof(float) * (size_t)pkv::kDecodeWaves * 2 * ncol * head_dim);
     pl.off_ml = off;
-    off = align256(off + sizeof(float) * (size_t)pkv::kDecodeWaves * 2 * group * 2);
+    off = align256(off + sizeof(float) * (size_t)pkv::kDecodeWaves * 2 * ncol * 2);
     pl.total = off;
     pl.prefill_tile_tokens = pkv::kPrefillRows / group;
     return pl;
@@ -114,6 +125,7 @@ template <typename T, int D>
 int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
                      const pkv::MergeParams& mp, const pkv::PrefillParams& pp, int max_seqlen_q,
                      int64_t total_q, int num_seqs, hipStream_t stream) {
+    // sequences with up to pl.wmax query tokens: plan, split-key pass, merge
     hipLaunchKernelGGL(pkv::decode_plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, stream, pl);
     if (int rc = hip_status("decode plan launch")) return rc;
     hipLaunchKernelGGL((pkv::decode_kernel<T, D>), dim3(pkv::kDecodeWaves), dim3(64), 0, stream, dp);
@@ -121,7 +133,7 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
     hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)), dim3(64),
                        0, stream, mp);
     if (int rc = hip_status("merge launch")) return rc;
-    if (max_seqlen_q > 1) {
+    if (max_seqlen_q > pl.wmax) {  // longer sequences: chunked prefill
         const long tiles = (total_q + pp.tile_tokens - 1) / pp.tile_tokens + num_seqs;
         hipLaunchKernelGGL((pkv::prefill_kernel<T, D>), dim3((unsigned)(tiles * pp.Hkv)),
                            dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
@@ -183,13 +195,13 @@ size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqle
                                     int max_seqlen_k, int num_q_heads, int num_kv_heads,
                                     int head_dim, int block_size, pkv_dtype_t dtype) {
     (void)total_q;
-    (void)max_seqlen_q;
     (void)max_seqlen_k;
     (void)dtype;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size != kBlock || num_q_heads % num_kv_heads)
         return 0;
-    return make_plan(num_seqs, num_kv_heads, head_dim, num_q_heads / num_kv_heads).total;
+    return make_plan(num_seqs, num_kv_heads, head_dim, num_q_heads / num_kv_heads,
+                     std::max(1, max_seqlen_q)).total;
 }
 
 int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -226,7 +238,8 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
         overlaps(out, io_bytes, v_pool, pool_bytes))
         return fail(PKV_E_ARG, "out must not alias q or the pools");
 
-    if (max_seqlen_q > 1 && (int64_t)max_seqlen_k > (int64_t)pkv::kMaxPrefillPages * kBlock)
+    if (max_seqlen_q > decode_window(num_q_heads / num_kv_heads, max_seqlen_q) &&
+        (int64_t)max_seqlen_k > (int64_t)pkv::kMaxPrefillPages * kBlock)
         return fail(PKV_E_UNSUPPORTED,
                     "steps with prefill chunks support contexts up to %d keys (max_seqlen_k %d)",
                     pkv::kMaxPrefillPages * kBlock, max_seqlen_k);
@@ -234,7 +247,7 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
         return fail(PKV_E_UNSUPPORTED, "num_seqs %d > %d is not supported", num_seqs,
                     pkv::kMaxDecodeSeqs);
     const int G = num_q_heads / num_kv_heads;
-    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, G);
+    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, G, max_seqlen_q);
     if (!workspace || workspace_bytes < pl.total)
         return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                     workspace ? workspace_bytes : (size_t)0, pl.total);
@@ -257,6 +270,7 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     plp.Hkv = num_kv_heads;
     plp.max_seqlen_k = max_seqlen_k;
     plp.max_blocks = max_blocks_per_seq;
+    plp.wmax = pl.wmax;
     plp.total_q = total_q;
     plp.pair_prefix = prefix;
     plp.portion_begin = pbegin;
@@ -276,6 +290,8 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     dp.Hq = num_q_heads;
     dp.Hkv = num_kv_heads;
     dp.G = G;
+    dp.gmagic = (65536 + G - 1) / G;
+    dp.ncol = G * pl.wmax;
     dp.num_blocks = num_blocks;
     dp.scale_log2 = scale_log2;
 
@@ -289,6 +305,7 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     mp.Hq = num_q_heads;
     mp.Hkv = num_kv_heads;
     mp.G = G;
+    mp.ncol = G * pl.wmax;
 
     pkv::PrefillParams pp;
     pp.out = out;
@@ -305,6 +322,7 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     pp.Hkv = num_kv_heads;
     pp.G = G;
     pp.tile_tokens = pl.prefill_tile_tokens;
+    pp.min_q = pl.wmax + 1;
     pp.max_seqlen_k = max_seqlen_k;
     pp.total_q = total_q;
     pp.num_blocks = num_blocks;

@@ -1,5 +1,5 @@
-// Chunked-prefill attention for sequences with two or more query tokens in
-// the step.
+// Chunked-prefill attention for sequences with more query tokens in the step
+// than the decode path takes (a chunk of a prompt).
 //
 // A prefill chunk is a dense contraction (vllm-metal v0.4.0 release post,
 // "The same stack on DGX Spark": a long prompt is one large matmul, bound by
@@ -54,6 +54,7 @@ struct PrefillParams {
     int Hkv;
     int G;
     int tile_tokens;   // query tokens per workgroup: floor(128 / G)
+    int min_q;         // sequences with fewer query tokens take the decode path
     int max_seqlen_k;
     int64_t total_q;
     int64_t num_blocks;
@@ -164,10 +165,10 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     constexpr int SPLIT = Gm::SPLIT;
     constexpr int NW = Gm::NW;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * Gm::STAGE];
-    __shared__ int32_t lds_bid[kMaxPrefillPages];
+    __shared__ __attribute__((aligned(8))) int32_t lds_bid[kMaxPrefillPages];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
@@ -189,7 +190,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     const int s = lo;
     int q0 = p.qsl[s];
     int n = p.qsl[s + 1] - q0;
-    if (q0 < 0 || q0 >= p.total_q || n < 2) return;
+    if (q0 < 0 || q0 >= p.total_q || n < p.min_q || n < 2) return;
     if (n > p.total_q - q0) n = (int)(p.total_q - q0);
     const int qt = bid - (q0 / BQ + s);
     const int tok0 = qt * BQ;
@@ -235,9 +236,10 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         }
     }
     {
+        // entries 2st, 2st + 1 are stage st's pages; an odd count repeats the last
         const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
-        for (int i = tid; i < npages; i += blockDim.x) {
-            const int32_t b = bt[first_page + i];
+        for (int i = tid; i < 2 * nstage; i += blockDim.x) {
+            const int32_t b = bt[first_page + min(i, npages - 1)];
             lds_bid[i] = (b >= 0 && b < p.num_blocks) ? b : 0;
         }
     }
@@ -260,11 +262,11 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         const int row = (blk % BPP) * Gm::ROWS_PER_BLOCK + lane / Gm::CPR;
         src_off[c] = row * Gm::RB + swz<Gm::CPR>(row, lane % Gm::CPR) * 16;
     }
-    auto issue_stage = [&](int st) {
-        const int pa = first_page + 2 * st;
-        const int pb = (pa + 1 <= last_page) ? pa + 1 : pa;
-        const int64_t ba = __builtin_amdgcn_readfirstlane(lds_bid[pa - first_page]);
-        const int64_t bb = __builtin_amdgcn_readfirstlane(lds_bid[pb - first_page]);
+    // block ids of stage st's two pages (read ahead of their use)
+    auto stage_ids = [&](int st) { return *reinterpret_cast<const int2*>(&lds_bid[2 * st]); };
+    auto issue_stage = [&](int st, int2 ids) {
+        const int64_t ba = __builtin_amdgcn_readfirstlane(ids.x);
+        const int64_t bb = __builtin_amdgcn_readfirstlane(ids.y);
         const uint8_t* kA = kpool + ba * page_stride + head_off;
         const uint8_t* kB = kpool + bb * page_stride + head_off;
         const uint8_t* vA = vpool + ba * page_stride + head_off;
@@ -319,26 +321,39 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         constexpr int SLOT = decltype(slot_tag)::value;
         const uint8_t* sb = lds + (SLOT >= 0 ? SLOT : dyn_slot) * Gm::STAGE;
         const int pa = first_page + 2 * st;
+        // ---- operands from LDS: K for the logits, and (bfloat16) V^T for the
+        // product, read up front so their latency overlaps the softmax
+        u32x4 kop[2][Gm::KCH];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int i = 0; i < Gm::KCH; ++i)
+                kop[x][i] = *reinterpret_cast<const u32x4*>(sb + x * Gm::PAGE + koff[i]);
+        u32x4 vop[kBF ? Gm::NT : 1];
+        if constexpr (kBF) {
+#pragma unroll
+            for (int t = 0; t < Gm::NT; ++t) {
+                const uint2 lo = lds_read_tr16(sb + 2 * Gm::PAGE + voff[t]);
+                const uint2 hi = lds_read_tr16(sb + 3 * Gm::PAGE + voff[t]);
+                vop[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        }
         // ---- S^T tiles: keys of page x as rows, this wavefront's rows as columns
         f32x4 sx[2][2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            u32x4 kop[Gm::KCH];
-#pragma unroll
-            for (int i = 0; i < Gm::KCH; ++i)
-                kop[i] = *reinterpret_cast<const u32x4*>(sb + x * Gm::PAGE + koff[i]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (kBF) {
 #pragma unroll
-                    for (int i = 0; i < Gm::KCH; ++i) sacc = mfma_bf16(kop[i], qop[nt][i], sacc);
+                    for (int i = 0; i < Gm::KCH; ++i) sacc = mfma_bf16(kop[x][i], qop[nt][i], sacc);
                 } else {
 #pragma unroll
                     for (int i = 0; i < Gm::KCH; ++i)
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            sacc = mfma_f32(__uint_as_float(kop[i][t]),
+                            sacc = mfma_f32(__uint_as_float(kop[x][i][t]),
                                             __uint_as_float(qop[nt][i][t]), sacc);
                 }
                 sx[nt][x] = sacc;
@@ -416,9 +431,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             }
 #pragma unroll
             for (int t = 0; t < Gm::NT; ++t) {
-                const uint2 lo = lds_read_tr16(sb + 2 * Gm::PAGE + voff[t]);
-                const uint2 hi = lds_read_tr16(sb + 3 * Gm::PAGE + voff[t]);
-                u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                u32x4 a = vop[t];
                 if constexpr (EDGE) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) a[q] &= keep[q];
@@ -454,6 +467,8 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     // of a row block.  Before the barrier this thread's loads of those stages
     // are complete; after it every wavefront is done with round rr - 1, whose
     // slots take the stages NS - SPLIT ahead.
+    // ids[j]: block ids of the stage the next round loads as its j-th
+    int2 ids[SPLIT];
     auto round = [&](auto edge_tag, auto slot_tag, int rr) {
         const int last_needed = min(rr * SPLIT + SPLIT - 1, nstage - 1);
         const int last_issued = min(rr * SPLIT + NS - SPLIT - 1, nstage - 1);
@@ -462,7 +477,10 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
 #pragma unroll
         for (int j = 0; j < SPLIT; ++j) {
             const int st = rr * SPLIT + NS - SPLIT + j;
-            if (st < nstage) issue_stage(st);
+            if (st < nstage) {
+                issue_stage(st, ids[j]);
+                if (st + SPLIT < nstage) ids[j] = stage_ids(st + SPLIT);
+            }
         }
         const int st = rr * SPLIT + half;
         if (st < nstage) compute(edge_tag, slot_tag, (rr * SPLIT) % NS, st);
@@ -470,7 +488,10 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
 
 #pragma unroll
     for (int st = 0; st < NS - SPLIT; ++st)
-        if (st < nstage) issue_stage(st);
+        if (st < nstage) issue_stage(st, stage_ids(st));
+#pragma unroll
+    for (int j = 0; j < SPLIT; ++j)
+        ids[j] = stage_ids(min(NS - SPLIT + j, nstage - 1));
 
     using Dyn = std::integral_constant<int, -1>;
     // Round 0 and every round past the interior take the masked path; interior

@@ -1,7 +1,8 @@
 """pkv_attention on the GPU against the float64 oracle over a sweep of shapes:
 group sizes 1-16, head_dim 64/128, float32 and bfloat16, decode contexts at
-page edges and across several splits, prefill chunks of 2 to 1000 tokens with
-and without cached context, mixed steps, left-padded steps; plus bitwise
+page edges and across several splits, speculative-verify windows of up to
+16 / G tokens, prefill chunks of 2 to 1000 tokens with and without cached
+context, mixed steps, left-padded steps; plus bitwise
 properties of the GPU path itself (physical page placement, run-to-run
 determinism, shared versus duplicated prefix pages) and a large packed step
 checked on sampled tokens.  Pools are NaN outside the valid rows."""
@@ -57,6 +58,40 @@ def test_prefill_and_mixed_sweep(G, D, dtype):
     lens = [b for _, b in PREFILL_SHAPES]
     st = W.build_step("prefill-sweep", lens, ql, 2 * G, 2, D, dtype, 200 + G * 7 + D)
     _run_full(st, f"prefill G={G} D={D}")
+
+
+WINDOW_LENS = [2, 15, 16, 17, 31, 33, 64, 65, 100, 257, 1000, 1600]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 5, 8, 16])
+def test_verify_window_sweep(G, D, dtype):
+    """Speculative-verify windows: sequences with 1..W query tokens (W = 16 // G)
+    take the decode path with a causal cap per window token; one sequence with
+    W + 1 tokens and one long chunk take the prefill path in the same step."""
+    wmax = 16 // G
+    ql = [1 + i % wmax for i in range(len(WINDOW_LENS))]
+    ql = [min(n, L) for n, L in zip(ql, WINDOW_LENS)]
+    lens = WINDOW_LENS + [40, 700]
+    ql = ql + [min(wmax + 1, 40), 90]
+    log(f"windows G={G} D={D} {dtype} q_lens={ql}")
+    st = W.build_step("window-sweep", lens, ql, 2 * G, 2, D, dtype, 700 + G * 7 + D)
+    _run_full(st, f"windows G={G} D={D}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("max_q", [2, 3, 4])
+def test_windows_only_step(max_q, dtype):
+    """A step of decodes and verify windows only (max_seqlen_q <= 16 // G): no
+    prefill launch; the window sizes the decode workspace."""
+    lens = [3000, 1, 4, 17, 512, 2049, 33, 5000]
+    ql = [max_q, 1, min(max_q, 4), 2, max_q, 1, max_q, 2]
+    st = W.build_step("windows-only", lens, ql, 16, 4, 128, dtype, 800 + max_q)
+    assert st.max_seqlen_q == max_q
+    _run_full(st, f"windows-only max_q={max_q}")
 
 
 @pytest.mark.gpu
