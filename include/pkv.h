@@ -126,9 +126,7 @@ size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqle
  *
  * Supported: dtype F32/BF16 (q, pools and out share it), head_dim 64 or 128,
  * block_size 16, num_q_heads % num_kv_heads == 0 and 1 <= group size <= 16,
- * num_seqs <= 16384, and max_seqlen_k <= 65536 when max_seqlen_q > W (a
- * prefill workgroup stages its block-table entries on chip); otherwise
- * PKV_E_UNSUPPORTED.
+ * and num_seqs <= 16384; otherwise PKV_E_UNSUPPORTED.
  * out must not alias q or the pools.  workspace must hold at least
  * pkv_attention_workspace_size(...) bytes (it may be NULL when that is 0).
  * num_seqs == 0 or total_q == 0 returns PKV_OK without launching.

@@ -135,8 +135,14 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
     if (int rc = hip_status("merge launch")) return rc;
     if (max_seqlen_q > pl.wmax) {  // longer sequences: chunked prefill
         const long tiles = (total_q + pp.tile_tokens - 1) / pp.tile_tokens + num_seqs;
-        hipLaunchKernelGGL((pkv::prefill_kernel<T, D>), dim3((unsigned)(tiles * pp.Hkv)),
-                           dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
+        // a tile's pages: at most ceil(max_seqlen_k / 16) + 1, rounded up to pairs
+        const bool long_ctx = ((long)pp.max_seqlen_k + kBlock - 1) / kBlock + 2 > pkv::kPrefillIdTable;
+        if (long_ctx)
+            hipLaunchKernelGGL((pkv::prefill_kernel<T, D, true>), dim3((unsigned)(tiles * pp.Hkv)),
+                               dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
+        else
+            hipLaunchKernelGGL((pkv::prefill_kernel<T, D, false>), dim3((unsigned)(tiles * pp.Hkv)),
+                               dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
         if (int rc = hip_status("prefill launch")) return rc;
     }
     return PKV_OK;
@@ -238,11 +244,6 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
         overlaps(out, io_bytes, v_pool, pool_bytes))
         return fail(PKV_E_ARG, "out must not alias q or the pools");
 
-    if (max_seqlen_q > decode_window(num_q_heads / num_kv_heads, max_seqlen_q) &&
-        (int64_t)max_seqlen_k > (int64_t)pkv::kMaxPrefillPages * kBlock)
-        return fail(PKV_E_UNSUPPORTED,
-                    "steps with prefill chunks support contexts up to %d keys (max_seqlen_k %d)",
-                    pkv::kMaxPrefillPages * kBlock, max_seqlen_k);
     if (num_seqs > pkv::kMaxDecodeSeqs)
         return fail(PKV_E_UNSUPPORTED, "num_seqs %d > %d is not supported", num_seqs,
                     pkv::kMaxDecodeSeqs);

@@ -23,14 +23,13 @@
 // Staging: pairs of KV pages (32 keys; K and V of two pages, 16 KiB for bf16
 // head_dim 128) go from HBM straight into a ring of kStages LDS buffers with
 // global->LDS loads, issued several rounds ahead of the stages being consumed,
-// one workgroup barrier per round.  Inside a buffer each 16-byte chunk of a row sits at
-// chunk ^ f(row), so the 16 key rows read for one K operand fall in distinct
-// banks.  V^T operands come from the transposing LDS read (ds_read_b64_tr_b16),
-// which hands each lane 4 consecutive keys of one column.  The workgroup's
-// block-table entries are staged in LDS once.  The sequence that owns a tile
-// is found by a binary search over query_start_loc ("Replacing attention,
-// reusing the rest": each threadgroup finds its request by binary search over
-// cu_seqlens).
+// one workgroup barrier per round.  Inside a buffer each 16-byte chunk of a
+// row sits at chunk ^ f(row), with f chosen per page kind (K or V) so that
+// the rows one read instruction touches fall in distinct banks.  V^T operands come from the transposing LDS read (ds_read_b64_tr_b16),
+// which hands each lane 4 consecutive keys of one column.  The sequence that
+// owns a tile is found by a binary search over query_start_loc ("Replacing
+// attention, reusing the rest": each threadgroup finds its request by binary
+// search over cu_seqlens).
 #pragma once
 
 #include <type_traits>
@@ -63,15 +62,34 @@ struct PrefillParams {
 
 constexpr int kPrefillRowBlocks = 4;                 // 32-row blocks per workgroup
 constexpr int kPrefillRows = 32 * kPrefillRowBlocks;
-constexpr int kMaxPrefillPages = 4096;  // block-table entries a workgroup stages (64K keys)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// 16 bytes from global memory straight into LDS: lane l writes block + 16 * l.
+// 16 bytes from global memory straight into LDS: lane l writes block + 16 * l
+// (block is wave-uniform; M0 holds its LDS address).  Written as inline
+// assembly so that the compiler does not treat later LDS reads of other ring
+// slots as possibly aliasing the transfer and wait for every load in flight:
+// the kernel orders these transfers itself, with explicit vmcnt waits and a
+// workgroup barrier before a staged buffer is read.
 __device__ __forceinline__ void load_to_lds16(const void* g, uint8_t* block) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)block, 16, 0, 0);
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_t*)block;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0), "v"(g)
+                 : "memory", "m0");
+}
+
+// Raises (1) or lowers (0) this wavefront's issue priority, pinned in place.
+// Around its matrix-core products a wavefront takes priority over the other
+// wavefront of its SIMD, so the two drift apart and one's softmax overlaps the
+// other's products.
+__device__ __forceinline__ void mfma_priority(int hi) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (hi) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Transposing LDS read: within each 16-lane group, lane i receives element
@@ -131,9 +149,18 @@ struct PrefillGeom {
                   "exchange area fits in the ring");
 };
 
-// Chunk position of row r's chunk c inside the LDS buffer.
+// Chunk position of row r's chunk c inside a staged LDS page.  K pages are
+// read one 16-byte chunk of each of 16 rows per instruction (the MFMA A
+// operand): XOR with the row spreads those over all banks.  V pages are read
+// by the transposing read, 8 bytes of 4 consecutive rows per 16 lanes: XOR
+// with twice the row keeps those 4 rows apart.  Both choices measured free of
+// bank conflicts on gfx950; the other way round each costs half the rate.
 template <int CPR>
-__device__ __forceinline__ int swz(int r, int c) {
+__device__ __forceinline__ int swz_k(int r, int c) {
+    return c ^ (r & (CPR - 1));
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int r, int c) {
     return c ^ ((((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1));
 }
 
@@ -157,7 +184,12 @@ __device__ __forceinline__ void unroll_rounds(F&& f) {
     }
 }
 
-template <typename T, int D>
+// Block-table entries a workgroup stages in LDS (contexts up to 64K keys);
+// longer contexts use the LONG variant, which reads them through the scalar
+// data cache instead.
+constexpr int kPrefillIdTable = 4096;
+
+template <typename T, int D, bool LONG>
 __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillParams p) {
     using Gm = PrefillGeom<T, D>;
     constexpr bool kBF = Gm::kBF;
@@ -165,7 +197,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     constexpr int SPLIT = Gm::SPLIT;
     constexpr int NW = Gm::NW;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * Gm::STAGE];
-    __shared__ __attribute__((aligned(8))) int32_t lds_bid[kMaxPrefillPages];
+    __shared__ __attribute__((aligned(8))) int32_t lds_bid[LONG ? 2 : kPrefillIdTable];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -200,7 +232,8 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
     const int pos_min = r.L - n + tok0;           // position of the tile's first token
     const int pos_max = pos_min + ntok - 1;       // ... and of its last
-    if (pos_max < r.a || pos_max / kPage - r.first_page >= kMaxPrefillPages) {
+    if (pos_max < r.a ||
+        (!LONG && 2 * ((pos_max / kPage - r.first_page + 2) / 2) > kPrefillIdTable)) {
         // every row sees no key (only with metadata outside the contract): write zeros
         for (int rr = tid; rr < ntok * p.G; rr += blockDim.x) {
             const int tok = rr / p.G, hh = rr % p.G;
@@ -235,15 +268,6 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             qop[nt][i] = rvalid[nt] ? v : u32x4{0, 0, 0, 0};
         }
     }
-    {
-        // entries 2st, 2st + 1 are stage st's pages; an odd count repeats the last
-        const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
-        for (int i = tid; i < 2 * nstage; i += blockDim.x) {
-            const int32_t b = bt[first_page + min(i, npages - 1)];
-            lds_bid[i] = (b >= 0 && b < p.num_blocks) ? b : 0;
-        }
-    }
-    __syncthreads();
 
     const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
     const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
@@ -260,13 +284,39 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     for (int c = 0; c < Gm::LPT; ++c) {
         const int blk = c * NW + wave;
         const int row = (blk % BPP) * Gm::ROWS_PER_BLOCK + lane / Gm::CPR;
-        src_off[c] = row * Gm::RB + swz<Gm::CPR>(row, lane % Gm::CPR) * 16;
+        const bool kbuf = blk / BPP < 2;   // buffers 0, 1 hold K, 2, 3 hold V
+        src_off[c] = row * Gm::RB + (kbuf ? swz_k<Gm::CPR>(row, lane % Gm::CPR)
+                                          : swz_v<Gm::CPR>(row, lane % Gm::CPR)) * 16;
     }
-    // block ids of stage st's two pages (read ahead of their use)
-    auto stage_ids = [&](int st) { return *reinterpret_cast<const int2*>(&lds_bid[2 * st]); };
+    // Block ids of stage st's two pages (an odd page count repeats the last
+    // page; ids outside the pool read page 0), fetched a round ahead of their
+    // use.  Up to 64K keys the workgroup stages its block-table entries in
+    // LDS once; beyond that (LONG) they are read through the scalar data cache
+    // (constant address space: the table is read-only and the index uniform),
+    // which is counted apart from the global->LDS transfers but shares the
+    // LDS counter, so it is slightly slower.
+    typedef __attribute__((address_space(4))) const int32_t cint32_t;
+    const cint32_t* bt_row =
+        (const cint32_t*)(p.block_tables + (int64_t)s * p.max_blocks + first_page);
+    if constexpr (!LONG) {
+        for (int i = tid; i < 2 * nstage; i += blockDim.x)
+            lds_bid[i] = p.block_tables[(int64_t)s * p.max_blocks + first_page + min(i, npages - 1)];
+        __syncthreads();
+    }
+    auto stage_ids = [&](int st) {
+        if constexpr (LONG) {
+            return int2{bt_row[2 * st], bt_row[min(2 * st + 1, npages - 1)]};
+        } else {
+            return *reinterpret_cast<const int2*>(&lds_bid[2 * st]);
+        }
+    };
     auto issue_stage = [&](int st, int2 ids) {
-        const int64_t ba = __builtin_amdgcn_readfirstlane(ids.x);
-        const int64_t bb = __builtin_amdgcn_readfirstlane(ids.y);
+        // wave-uniform ids (LDS values are made scalar), so the page
+        // addresses are computed on the scalar unit
+        const int ia = LONG ? ids.x : __builtin_amdgcn_readfirstlane(ids.x);
+        const int ib = LONG ? ids.y : __builtin_amdgcn_readfirstlane(ids.y);
+        const int64_t ba = (ia >= 0 && ia < p.num_blocks) ? ia : 0;
+        const int64_t bb = (ib >= 0 && ib < p.num_blocks) ? ib : 0;
         const uint8_t* kA = kpool + ba * page_stride + head_off;
         const uint8_t* kB = kpool + bb * page_stride + head_off;
         const uint8_t* vA = vpool + ba * page_stride + head_off;
@@ -298,14 +348,14 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     int koff[Gm::KCH];  // K operand: row col, chunk 4i + grp
 #pragma unroll
     for (int i = 0; i < Gm::KCH; ++i)
-        koff[i] = hoff + col * Gm::RB + swz<Gm::CPR>(col, 4 * i + grp) * 16;
+        koff[i] = hoff + col * Gm::RB + swz_k<Gm::CPR>(col, 4 * i + grp) * 16;
     int voff[Gm::NT];   // bf16 V^T: row 4grp + col/4, columns 16t + 4(col%4) .. +3
     {
         const int vrow = 4 * grp + (col >> 2);
         const int vsub = (col & 3) * 8;
 #pragma unroll
         for (int t = 0; t < Gm::NT; ++t)
-            voff[t] = hoff + vrow * Gm::RB + swz<Gm::CPR>(vrow, 2 * t + (vsub >> 4)) * 16 +
+            voff[t] = hoff + vrow * Gm::RB + swz_v<Gm::CPR>(vrow, 2 * t + (vsub >> 4)) * 16 +
                       (vsub & 15);
     }
 
@@ -338,6 +388,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                 vop[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
             }
         }
+        mfma_priority(1);
         // ---- S^T tiles: keys of page x as rows, this wavefront's rows as columns
         f32x4 sx[2][2];
 #pragma unroll
@@ -359,6 +410,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                 sx[nt][x] = sacc;
             }
         }
+        mfma_priority(0);
         bool kval[8];
         if constexpr (EDGE) {
 #pragma unroll
@@ -418,6 +470,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                                pack_bf16(pv[nt][4], pv[nt][5]), pack_bf16(pv[nt][6], pv[nt][7])};
         }
 
+        mfma_priority(1);
         // ---- O^T += V^T P^T, and the column sums of P
         if constexpr (kBF) {
             const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
@@ -453,7 +506,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                         const int dcol = t * 16 + col;
                         float v = *reinterpret_cast<const float*>(
                             sb + hoff + (2 + x) * Gm::PAGE + key * Gm::RB +
-                            swz<Gm::CPR>(key, dcol >> 2) * 16 + (dcol & 3) * 4);
+                            swz_v<Gm::CPR>(key, dcol >> 2) * 16 + (dcol & 3) * 4);
                         if constexpr (EDGE) v = kval[x * 4 + u] ? v : 0.f;
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt)
@@ -461,6 +514,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                     }
                 }
         }
+        mfma_priority(0);
     };
 
     // Round rr: stages rr * SPLIT .. rr * SPLIT + SPLIT - 1, one per wavefront
@@ -477,15 +531,33 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
 #pragma unroll
         for (int j = 0; j < SPLIT; ++j) {
             const int st = rr * SPLIT + NS - SPLIT + j;
-            if (st < nstage) {
-                issue_stage(st, ids[j]);
-                if (st + SPLIT < nstage) ids[j] = stage_ids(st + SPLIT);
+            if (st < nstage) issue_stage(st, ids[j]);
+        }
+        if constexpr (!LONG) {
+#pragma unroll
+            for (int j = 0; j < SPLIT; ++j) {
+                const int nx = rr * SPLIT + NS + j;
+                if (nx < nstage) ids[j] = stage_ids(nx);
             }
         }
         const int st = rr * SPLIT + half;
         if (st < nstage) compute(edge_tag, slot_tag, (rr * SPLIT) % NS, st);
+        if constexpr (LONG) {
+            // the next round's block ids, fetched after this round's LDS reads
+            // so that their scalar-cache latency overlaps the barrier rather
+            // than the reads (both are counted by lgkmcnt)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < SPLIT; ++j) {
+                const int nx = rr * SPLIT + NS + j;
+                if (nx < nstage) ids[j] = stage_ids(nx);
+            }
+        }
     };
 
+    // the query operands have arrived before any staged load is issued, so
+    // the vmcnt waits below count staged loads only
+    wait_vmcnt<0>();
 #pragma unroll
     for (int st = 0; st < NS - SPLIT; ++st)
         if (st < nstage) issue_stage(st, stage_ids(st));

@@ -172,6 +172,16 @@ def test_packed_30000_5000_10_step_on_sampled_tokens():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+def test_long_context_prefill_chunk(dtype):
+    """A 40-token chunk at the end of a 100,000-key context and a decode over
+    70,001 keys in one step: contexts far past 65,536 keys on both paths."""
+    st = W.build_step("long-context", [100000, 70001], [40, 1], 4, 1, 64, dtype, 900)
+    assert st.max_seqlen_k > 65536
+    _run_full(st, "long context")
+
+
+@pytest.mark.gpu
 def test_workspace_reuse_and_explicit_out():
     st = W.config_step(2)
     q = st.make_q("cpu").cuda()
