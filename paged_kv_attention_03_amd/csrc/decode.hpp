@@ -50,6 +50,8 @@ constexpr int kDecodeWaves = 2048;     // persistent decode waves (8 per CU on 2
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxDecodeSeqs = 16384;  // sequences the plan kernel can hold in LDS
 constexpr int kWindowPages = 256;      // block-table entries staged per window
+constexpr int kInlinePlanSeqs = 512;   // up to this many sequences each decode wave
+                                       // plans its own pieces (no plan kernel)
 
 // A wave's piece of one (sequence, kv head) segment: page pairs [pi0, pi1).
 struct Portion {
@@ -82,8 +84,19 @@ struct DecodeParams {
     const void* k_pool;
     const void* v_pool;
     const int32_t* block_tables;
-    const int32_t* portion_begin;
-    const Portion* portions;
+    const int32_t* portion_begin;  // plan-kernel mode only
+    const Portion* portions;       // plan-kernel mode only
+    // inline-plan mode (num_seqs <= kInlinePlanSeqs): every wave derives its
+    // pieces from the step metadata; wave 0 also writes pair_prefix
+    int inline_plan;
+    const int32_t* seq_lens;
+    const int32_t* qsl;
+    const int32_t* kv_start;
+    int num_seqs;
+    int max_seqlen_k;
+    int wmax;
+    int64_t total_q;
+    int32_t* pair_prefix;
     float* ws_o;    // [kDecodeWaves * 2][ncol][D] unnormalised partial outputs
     float* ws_ml;   // [kDecodeWaves * 2][ncol][2] (running max in log2 units, sum)
     int max_blocks;
@@ -122,6 +135,18 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// Page pairs a sequence contributes to the decode path: its visible pages
+// [first_page, end_page) in pairs, if it has 1..wmax query tokens, else 0.
+__device__ __forceinline__ int decode_pairs(const int32_t* qsl, const int32_t* seq_lens,
+                                            const int32_t* kv_start, int s, int wmax,
+                                            int64_t total_q, int max_seqlen_k, int max_blocks) {
+    const int q0 = qsl[s];
+    const int nq = qsl[s + 1] - q0;
+    const bool dec = nq >= 1 && nq <= wmax && q0 >= 0 && q0 <= total_q - nq;
+    const SeqRange r = seq_range(seq_lens, kv_start, s, max_seqlen_k, max_blocks);
+    return dec ? (r.end_page - r.first_page + 1) / 2 : 0;
+}
+
 // In-place exclusive scan of a[0..n) by a 1024-thread block; a[n] = total.
 __device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
     const int t = threadIdx.x;
@@ -155,13 +180,9 @@ __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(PlanParams p)
     __shared__ int32_t tmp[kPlanThreads];
     const int t = threadIdx.x;
     const int S = p.num_seqs;
-    for (int s = t; s < S; s += kPlanThreads) {
-        const int q0 = p.qsl[s];
-        const int nq = p.qsl[s + 1] - q0;
-        const bool dec = nq >= 1 && nq <= p.wmax && q0 >= 0 && q0 <= p.total_q - nq;
-        const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
-        C[s] = dec ? (r.end_page - r.first_page + 1) / 2 : 0;
-    }
+    for (int s = t; s < S; s += kPlanThreads)
+        C[s] = decode_pairs(p.qsl, p.seq_lens, p.kv_start, s, p.wmax, p.total_q, p.max_seqlen_k,
+                            p.max_blocks);
     __syncthreads();
     block_exclusive_scan(C, S, tmp);
     const int64_t U = (int64_t)p.Hkv * C[S];
@@ -242,14 +263,68 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * Gm::PAGE_LDS];
     __shared__ int32_t lds_bid[kWindowPages];
     __shared__ Portion lds_port[kWave];  // this batch's segment pieces
+    __shared__ int32_t lds_pref[kInlinePlanSeqs + 1];
 
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int w = blockIdx.x;
-    const int pb = p.portion_begin[w];
-    const int pe = p.portion_begin[w + 1];
-    if (pb >= pe) return;
+    const bool inl = p.inline_plan != 0;
+    const int S = p.num_seqs;
+    int pb = 0, pe = 0;       // plan-kernel mode: this wave's pieces
+    int64_t u0 = 0, u1 = 0;   // inline mode: this wave's units [u0, u1)
+    if (inl) {
+        // page pairs of every sequence and their exclusive prefix, in LDS
+        const int per = (S + kWave - 1) / kWave;
+        const int s_lo = min(S, lane * per), s_hi = min(S, s_lo + per);
+        int sum = 0;
+        for (int s = s_lo; s < s_hi; ++s) {
+            const int c = decode_pairs(p.qsl, p.seq_lens, p.kv_start, s, p.wmax, p.total_q,
+                                       p.max_seqlen_k, p.max_blocks);
+            lds_pref[s] = c;
+            sum += c;
+        }
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        int run = incl - sum;
+        for (int s = s_lo; s < s_hi; ++s) {
+            const int c = lds_pref[s];
+            lds_pref[s] = run;
+            run += c;
+        }
+        if (lane == kWave - 1) lds_pref[S] = incl;
+        wave_lds_fence();
+        if (w == 0)
+            for (int s = lane; s <= S; s += kWave) p.pair_prefix[s] = lds_pref[s];
+        const int64_t U = (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(lds_pref[S]);
+        u0 = wave_start(w, U);
+        u1 = wave_start(w + 1, U);
+        if (u0 >= u1) return;
+    } else {
+        pb = p.portion_begin[w];
+        pe = p.portion_begin[w + 1];
+        if (pb >= pe) return;
+    }
+    auto pref = [&](int s) { return __builtin_amdgcn_readfirstlane(lds_pref[s]); };
+    // inline mode: the walk over the segments that meet [u0, u1) -- sequence
+    // ws, kv head wg, ws's pairs wc, pieces emitted so far
+    int ws = 0, wg = 0, wcount = 0;
+    int64_t wc = 0;
+    bool wdone = !inl;
+    if (inl) {
+        int lo = 0, hi = S - 1;  // largest s with Hkv * P[s] <= u0 (then P[s+1] > P[s])
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)p.Hkv * pref(mid) <= u0) lo = mid; else hi = mid - 1;
+        }
+        ws = lo;
+        wc = pref(ws + 1) - pref(ws);
+        wg = (int)((u0 - (int64_t)p.Hkv * pref(ws)) / wc);
+    }
 
     const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
     const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
@@ -265,19 +340,51 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
         return (col * m) >> 16;
     };
 
-    for (int b0 = pb; b0 < pe; b0 += kWave) {
-        // ---- this batch's segment pieces, one per lane
-        const int n = min(kWave, pe - b0);
-        int npairs = 0;
+    for (int b0 = pb;;) {
+        // ---- this batch's segment pieces (up to 64) into lds_port
+        int n = 0, npairs = 0;
         wave_lds_fence();  // the previous batch is done with lds_port
-        if (lane < n) {
-            const Portion q = p.portions[b0 + lane];
-            lds_port[lane] = q;
-            npairs = q.pi1 - q.pi0;
+        if (!inl) {
+            if (b0 >= pe) break;
+            n = min(kWave, pe - b0);
+            if (lane < n) {
+                const Portion q = p.portions[b0 + lane];
+                lds_port[lane] = q;
+                npairs = q.pi1 - q.pi0;
+            }
+            b0 += n;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) npairs += __shfl_xor(npairs, off);
+        } else {
+            if (wdone) break;
+            while (n < kWave && !wdone) {
+                const int64_t seg0 = (int64_t)p.Hkv * pref(ws) + (int64_t)wg * wc;
+                const int64_t seg1 = seg0 + wc;
+                Portion q;
+                q.s = ws;
+                q.g = wg;
+                q.pi0 = (int32_t)(max(u0, seg0) - seg0);
+                q.pi1 = (int32_t)(min(u1, seg1) - seg0);
+                q.slot = (seg0 >= u0 && seg1 <= u1) ? -1 : w * 2 + (wcount == 0 ? 0 : 1);
+                q.q0 = p.qsl[ws];
+                q.nq = p.qsl[ws + 1] - q.q0;
+                const SeqRange r = seq_range(p.seq_lens, p.kv_start, ws, p.max_seqlen_k, p.max_blocks);
+                q.kv_lo = r.a;
+                q.kv_hi = r.L;
+                if (lane == 0) lds_port[n] = q;
+                npairs += q.pi1 - q.pi0;
+                ++n;
+                ++wcount;
+                if (seg1 >= u1) {
+                    wdone = true;
+                } else if (++wg == p.Hkv) {
+                    wg = 0;
+                    do { ++ws; } while (pref(ws + 1) == pref(ws));
+                    wc = pref(ws + 1) - pref(ws);
+                }
+            }
         }
         wave_lds_fence();
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) npairs += __shfl_xor(npairs, off);
         const int K = npairs;
         // a field of piece idx (uniform), read back from LDS into a scalar register
 #define PKV_FIELD(name, idx) __builtin_amdgcn_readfirstlane(lds_port[idx].name)

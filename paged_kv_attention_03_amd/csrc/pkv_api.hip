@@ -125,9 +125,12 @@ template <typename T, int D>
 int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
                      const pkv::MergeParams& mp, const pkv::PrefillParams& pp, int max_seqlen_q,
                      int64_t total_q, int num_seqs, hipStream_t stream) {
-    // sequences with up to pl.wmax query tokens: plan, split-key pass, merge
-    hipLaunchKernelGGL(pkv::decode_plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, stream, pl);
-    if (int rc = hip_status("decode plan launch")) return rc;
+    // sequences with up to pl.wmax query tokens: plan (large batches only;
+    // otherwise each decode wave plans its own pieces), split-key pass, merge
+    if (!dp.inline_plan) {
+        hipLaunchKernelGGL(pkv::decode_plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, stream, pl);
+        if (int rc = hip_status("decode plan launch")) return rc;
+    }
     hipLaunchKernelGGL((pkv::decode_kernel<T, D>), dim3(pkv::kDecodeWaves), dim3(64), 0, stream, dp);
     if (int rc = hip_status("decode launch")) return rc;
     hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)), dim3(64),
@@ -294,6 +297,15 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
     dp.gmagic = (65536 + G - 1) / G;
     dp.ncol = G * pl.wmax;
     dp.num_blocks = num_blocks;
+    dp.inline_plan = num_seqs <= pkv::kInlinePlanSeqs ? 1 : 0;
+    dp.seq_lens = seq_lens;
+    dp.qsl = query_start_loc;
+    dp.kv_start = kv_start;
+    dp.num_seqs = num_seqs;
+    dp.max_seqlen_k = max_seqlen_k;
+    dp.wmax = pl.wmax;
+    dp.total_q = total_q;
+    dp.pair_prefix = prefix;
     dp.scale_log2 = scale_log2;
 
     pkv::MergeParams mp;

@@ -173,6 +173,22 @@ def test_packed_30000_5000_10_step_on_sampled_tokens():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("num_seqs", [512, 513, 1500])
+def test_many_sequences(num_seqs, dtype):
+    """Batches at and past the size where the decode waves stop planning their
+    own pieces and a plan kernel does it: ragged short contexts, decodes and
+    2-token windows, one prefill chunk."""
+    rng = np.random.default_rng(num_seqs)
+    lens = rng.integers(1, 300, size=num_seqs).tolist()
+    ql = [2 if (i % 7 == 3 and L >= 2) else 1 for i, L in enumerate(lens)]
+    lens[5], ql[5] = 400, 37
+    log(f"many sequences: {num_seqs} {dtype}")
+    st = W.build_step("many-seqs", lens, ql, 16, 4, 64, dtype, 950 + num_seqs)
+    _run_full(st, f"{num_seqs} sequences")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
 def test_long_context_prefill_chunk(dtype):
     """A 40-token chunk at the end of a 100,000-key context and a decode over
     70,001 keys in one step: contexts far past 65,536 keys on both paths."""
