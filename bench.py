@@ -328,7 +328,7 @@ def bench_single(k, args):
         "device_copy_gbs": copy_gbs,
         "copy_frac": gbs / copy_gbs,
         "packed_step_tokens_per_s": st.total_q / wall,
-        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_plan_kernel + decode_kernel + merge_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"decode_{st.name}"),
@@ -396,7 +396,7 @@ def bench_agent(k, args):
                    "page_size": 16, "logical_kv_bytes_per_step": logical,
                    "unique_kv_bytes_per_step": unique},
         "packed_step_tokens_per_s": b.num_seqs / wall,
-        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_plan_kernel + decode_kernel + merge_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
                      "achieved": unique / attn / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": unique / attn / 1e9 / HBM_PEAK_GBS, "traffic": None,
                      "launch_ms_mean": attn * 1e3, "algorithmic_bytes_per_launch": unique},
