@@ -273,6 +273,36 @@ def extra_windows(steps: int, warmup: int):
     return res
 
 
+def extra_pool(steps: int = 2000):
+    """Host-side pool manager on the large decode batch's shape: 128 sequences
+    of U[4096, 32768] tokens in a pool of 1.25x their pages.  Host time
+    (microseconds, one thread) of one step's slots (one slot per sequence) and
+    of exporting all 128 block-table rows."""
+    lens = np.random.default_rng(5000).integers(4096, 32768, size=128, endpoint=True)
+    bs = 16
+    width = int((lens.max() + steps + bs - 1) // bs) + 1
+    nb = int(1.25 * sum((int(x) + steps + bs - 1) // bs for x in lens))
+    pool = pkv.PagePool(nb, bs, 128, width)
+    for s_, n in enumerate(lens):
+        pool.add_seq(s_)
+        pool.append(s_, int(n))
+    seqs = list(range(128))
+    ones = [1] * 128
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pool.append_batch(seqs, ones)
+    t_app = (time.perf_counter() - t0) / steps
+    t0 = time.perf_counter()
+    for _ in range(steps // 10):
+        pool.block_tables(seqs, width)
+    t_bt = (time.perf_counter() - t0) / (steps // 10)
+    pool.close()
+    return {"workload": "pool-manager-128seq", "append_us_per_step": t_app * 1e6,
+            "block_tables_us": t_bt * 1e6, "table_width": width,
+            "note": "host time through the Python binding: one pkv_pool_append_batch per "
+                    "step (128 slots); one full pkv_pool_block_tables export"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +370,7 @@ def bench_single(k, args):
     if not args.no_extra and k != 3:
         rec["extra"] = extra_prefill(min(args.steps, 20), args.warmup)
         rec["extra"]["verify_windows"] = extra_windows(min(args.steps, 20), args.warmup)
+        rec["extra"]["pool_manager"] = extra_pool()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(st)
     return rec

@@ -15,8 +15,10 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless the argument says "host".
- *   - All memory is owned by the caller.  The library allocates nothing and
- *     keeps no state between calls except the thread-local error text.
+ *   - All memory is owned by the caller.  The device calls allocate nothing and
+ *     keep no state between calls except the thread-local error text.  The
+ *     host-side pool manager (pkv_pool_*) keeps its page tables in host memory
+ *     it owns, between pkv_pool_create and pkv_pool_destroy.
  *   - Calls only enqueue kernels on `stream` (a hipStream_t; NULL is the null
  *     stream) and never synchronise, so they can be captured in a HIP graph.
  *   - Return PKV_OK (0) or a negative PKV_E_* code; the reason is available
@@ -64,7 +66,8 @@ enum {
     PKV_E_UNSUPPORTED = -2, /* valid but not built: head_dim, block_size, dtype, group size */
     PKV_E_WORKSPACE = -3,   /* workspace missing or smaller than required */
     PKV_E_HIP = -4,         /* the HIP runtime reported an error at launch */
-    PKV_E_METADATA = -5     /* pkv_check_*: host metadata violates the contract */
+    PKV_E_METADATA = -5,    /* pkv_check_*: host metadata violates the contract */
+    PKV_E_NOMEM = -6        /* pkv_pool_*: too few free pages; nothing was changed */
 };
 
 /*
@@ -163,6 +166,93 @@ int pkv_check_slots(const int64_t *slot_mapping, int64_t num_tokens, int block_s
 /* Text of the last error on the calling thread ("" if none).  Valid until the
  * next pkv_* call on the same thread. */
 const char *pkv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Host-side pool manager.
+ *
+ * Bookkeeping for a KV pool of num_blocks pages reserved once at startup and
+ * serving every request: admission is checked against its free pages, so load
+ * changes the queue rather than the memory footprint (vllm-metal v0.4.0
+ * release post, "Set a predictable memory budget").  Sequences forked from a
+ * common prefix hold the same physical pages (reference counts); a sequence
+ * about to write into a page it shares first moves to a private copy of that
+ * page (copy-on-write), so pages shared by several sequences are only read,
+ * as pkv_append requires ("Prefix caching on hybrid models": rows are written
+ * in place).  The manager produces slot_mapping, block-table rows and
+ * seq_lens for the device calls above; it never touches device memory itself
+ * (pkv_copy_blocks performs the page copies it asks for).  All pointers of
+ * pkv_pool_* are HOST pointers.  A pool is not thread-safe: one host thread
+ * drives it.  Sequence ids are in [0, max_seqs).
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_pool pkv_pool_t;
+
+/* Creates a manager for num_blocks pages of block_size tokens; a sequence may
+ * hold at most max_blocks_per_seq pages.  Returns NULL on invalid sizes (the
+ * reason in pkv_last_error()). */
+pkv_pool_t *pkv_pool_create(int64_t num_blocks, int block_size, int max_seqs,
+                            int max_blocks_per_seq);
+void pkv_pool_destroy(pkv_pool_t *pool);
+
+/* Free pages, and whether a new sequence of num_tokens tokens fits now
+ * (1 / 0; -1 for a NULL pool). */
+int64_t pkv_pool_free_blocks(const pkv_pool_t *pool);
+int pkv_pool_can_admit(const pkv_pool_t *pool, int64_t num_tokens);
+
+/* Starts an empty sequence; PKV_E_ARG if seq is out of range or live. */
+int pkv_pool_add_seq(pkv_pool_t *pool, int seq);
+
+/* Starts sequence child as the first shared_tokens tokens of parent, on the
+ * parent's pages (no copy; 0 <= shared_tokens <= the parent's length). */
+int pkv_pool_fork(pkv_pool_t *pool, int parent, int child, int64_t shared_tokens);
+
+/* Reserves num_tokens more tokens at the end of seq and writes their slots
+ * (page * block_size + offset, token order) to slots[0..num_tokens).  If the
+ * sequence's last page is partly filled and shared, the sequence first moves
+ * to a fresh page: the (source, destination) page ids are written to
+ * cow_src[0] / cow_dst[0] and *num_cow = 1 (else 0); the caller copies those
+ * pages on the device (pkv_copy_blocks) before appending this step's rows.
+ * cow_src, cow_dst and num_cow may be NULL only when no copy can be needed.
+ * PKV_E_NOMEM if the free pages do not suffice, PKV_E_ARG if the sequence
+ * would exceed max_blocks_per_seq; in both cases nothing changes. */
+int pkv_pool_append(pkv_pool_t *pool, int seq, int64_t num_tokens, int64_t *slots,
+                    int32_t *cow_src, int32_t *cow_dst, int *num_cow);
+
+/* pkv_pool_append for num_seqs distinct sequences at once (one engine step):
+ * counts[i] tokens for seqs[i]; their slots are written back to back to slots
+ * in the order given (sum of counts entries), copy-on-write pairs to
+ * cow_src / cow_dst (room for num_seqs entries each), their number to
+ * *num_cow.  All-or-nothing: PKV_E_ARG (a sequence not live, listed twice or
+ * past max_blocks_per_seq) or PKV_E_NOMEM leaves the pool unchanged. */
+int pkv_pool_append_batch(pkv_pool_t *pool, const int *seqs, const int64_t *counts,
+                          int num_seqs, int64_t *slots, int32_t *cow_src, int32_t *cow_dst,
+                          int *num_cow);
+
+/* Drops the tokens of seq past new_len (for example the rejected draft tokens
+ * of a speculative-verify window); pages no longer used are released. */
+int pkv_pool_truncate(pkv_pool_t *pool, int seq, int64_t new_len);
+
+/* Ends seq and releases its pages (a shared page returns to the free list
+ * when its last holder releases it). */
+int pkv_pool_free_seq(pkv_pool_t *pool, int seq);
+
+/* Length of seq in tokens, or -1 if it is not live. */
+int64_t pkv_pool_seq_len(const pkv_pool_t *pool, int seq);
+
+/* Block-table rows and lengths of seqs[0..num_seqs): table is
+ * [num_seqs][width] int32, entries past a sequence's pages set to -1;
+ * seq_lens[i] is its length (may be NULL).  PKV_E_ARG if a sequence is not
+ * live or holds more than width pages. */
+int pkv_pool_block_tables(const pkv_pool_t *pool, const int *seqs, int num_seqs, int32_t *table,
+                          int width, int32_t *seq_lens);
+
+/* DEVICE call: copies whole pages src[i] -> dst[i] (K and V, every kv head),
+ * i < num_pairs; src and dst are device int32 arrays; pairs naming a page
+ * outside [0, num_blocks) are skipped.  Destinations must be distinct and must
+ * not be sources.  Pool layout and dtypes as for pkv_append.  num_pairs == 0
+ * returns PKV_OK without launching. */
+int pkv_copy_blocks(void *k_pool, void *v_pool, const int32_t *src, const int32_t *dst,
+                    int64_t num_pairs, int num_kv_heads, int head_dim, int block_size,
+                    int64_t num_blocks, pkv_dtype_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "PKV_F32", "PKV_BF16", "PkvError", "pkv_append", "pkv_attention",
     "pkv_attention_workspace_size", "pkv_check_metadata", "pkv_check_slots", "pkv_last_error",
-    "library_path", "load_library",
+    "pkv_copy_blocks", "PagePool", "library_path", "load_library",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,7 @@ PKV_E_UNSUPPORTED = -2
 PKV_E_WORKSPACE = -3
 PKV_E_HIP = -4
 PKV_E_METADATA = -5
+PKV_E_NOMEM = -6
 
 _lib = None
 
@@ -74,6 +75,32 @@ def load_library():
     lib.pkv_check_slots.restype = i32
     lib.pkv_last_error.argtypes = []
     lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_pool_create.argtypes = [i64, i32, i32, i32]
+    lib.pkv_pool_create.restype = vp
+    lib.pkv_pool_destroy.argtypes = [vp]
+    lib.pkv_pool_destroy.restype = None
+    lib.pkv_pool_free_blocks.argtypes = [vp]
+    lib.pkv_pool_free_blocks.restype = i64
+    lib.pkv_pool_can_admit.argtypes = [vp, i64]
+    lib.pkv_pool_can_admit.restype = i32
+    lib.pkv_pool_add_seq.argtypes = [vp, i32]
+    lib.pkv_pool_add_seq.restype = i32
+    lib.pkv_pool_fork.argtypes = [vp, i32, i32, i64]
+    lib.pkv_pool_fork.restype = i32
+    lib.pkv_pool_append.argtypes = [vp, i32, i64, vp, vp, vp, vp]
+    lib.pkv_pool_append.restype = i32
+    lib.pkv_pool_append_batch.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp]
+    lib.pkv_pool_append_batch.restype = i32
+    lib.pkv_pool_truncate.argtypes = [vp, i32, i64]
+    lib.pkv_pool_truncate.restype = i32
+    lib.pkv_pool_free_seq.argtypes = [vp, i32]
+    lib.pkv_pool_free_seq.restype = i32
+    lib.pkv_pool_seq_len.argtypes = [vp, i32]
+    lib.pkv_pool_seq_len.restype = i64
+    lib.pkv_pool_block_tables.argtypes = [vp, vp, i32, vp, i32, vp]
+    lib.pkv_pool_block_tables.restype = i32
+    lib.pkv_copy_blocks.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
+    lib.pkv_copy_blocks.restype = i32
     _lib = lib
     return lib
 
@@ -222,3 +249,107 @@ def pkv_check_slots(slot_mapping, block_size: int, num_blocks: int) -> None:
         slot_mapping = slot_mapping.detach().cpu().numpy()
     sm = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64))
     _raise(load_library().pkv_check_slots(sm.ctypes.data, sm.shape[0], block_size, num_blocks))
+
+
+def pkv_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, src: torch.Tensor,
+                    dst: torch.Tensor, stream=None) -> None:
+    """Copy whole pages src[i] -> dst[i] (K and V) inside pools
+    [num_blocks, Hkv, bs, D]; src/dst are device int32 [n]."""
+    lib = load_library()
+    dt = _dtype_code(k_pool.dtype)
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("pools must be [num_blocks, Hkv, block_size, D] and equal")
+    nb, hkv, bs, d = k_pool.shape
+    if src.dim() != 1 or dst.shape != src.shape:
+        raise ValueError("src and dst must be [n]")
+    n = src.shape[0]
+    _raise(lib.pkv_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+                               _dev(src, "src", torch.int32), _dev(dst, "dst", torch.int32),
+                               n, hkv, d, bs, nb, dt, _stream(k_pool.device, stream)))
+
+
+class PagePool:
+    """Host-side manager of a KV pool of ``num_blocks`` pages reserved once
+    (the ``pkv_pool_*`` C calls): slots for new rows, block tables, shared
+    prefixes by reference count with copy-on-write, admission against the
+    free pages.  Host arrays only; device page copies are the caller's
+    (``pkv_copy_blocks``)."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int,
+                 max_blocks_per_seq: int):
+        self._lib = load_library()
+        h = self._lib.pkv_pool_create(num_blocks, block_size, max_seqs, max_blocks_per_seq)
+        if not h:
+            raise PkvError(PKV_E_ARG, pkv_last_error())
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.max_seqs = max_seqs
+        self.max_blocks_per_seq = max_blocks_per_seq
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def free_blocks(self) -> int:
+        return int(self._lib.pkv_pool_free_blocks(self._h))
+
+    def can_admit(self, num_tokens: int) -> bool:
+        return self._lib.pkv_pool_can_admit(self._h, num_tokens) == 1
+
+    def add_seq(self, seq: int) -> None:
+        _raise(self._lib.pkv_pool_add_seq(self._h, seq))
+
+    def fork(self, parent: int, child: int, shared_tokens: int) -> None:
+        _raise(self._lib.pkv_pool_fork(self._h, parent, child, shared_tokens))
+
+    def append(self, seq: int, num_tokens: int):
+        """Reserve num_tokens slots; returns (slots int64 [n], copies) where
+        copies is a list of (src_page, dst_page) to copy before appending."""
+        import numpy as np
+        slots = np.empty(max(num_tokens, 1), dtype=np.int64)
+        cs = np.zeros(1, dtype=np.int32)
+        cd = np.zeros(1, dtype=np.int32)
+        nc = ctypes.c_int(0)
+        _raise(self._lib.pkv_pool_append(self._h, seq, num_tokens, slots.ctypes.data,
+                                         cs.ctypes.data, cd.ctypes.data, ctypes.byref(nc)))
+        return slots[:num_tokens], [(int(cs[0]), int(cd[0]))] if nc.value else []
+
+    def append_batch(self, seqs, counts):
+        """append() for distinct sequences in one call; returns (slots int64
+        [sum(counts)] in the order given, copies [(src, dst)])."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int64))
+        slots = np.empty(max(int(cnt.sum()), 1), dtype=np.int64)
+        cs = np.zeros(max(len(ids), 1), dtype=np.int32)
+        cd = np.zeros(max(len(ids), 1), dtype=np.int32)
+        nc = ctypes.c_int(0)
+        _raise(self._lib.pkv_pool_append_batch(self._h, ids.ctypes.data, cnt.ctypes.data,
+                                               len(ids), slots.ctypes.data, cs.ctypes.data,
+                                               cd.ctypes.data, ctypes.byref(nc)))
+        return slots[:int(cnt.sum())], [(int(cs[i]), int(cd[i])) for i in range(nc.value)]
+
+    def truncate(self, seq: int, new_len: int) -> None:
+        _raise(self._lib.pkv_pool_truncate(self._h, seq, new_len))
+
+    def free_seq(self, seq: int) -> None:
+        _raise(self._lib.pkv_pool_free_seq(self._h, seq))
+
+    def seq_len(self, seq: int) -> int:
+        return int(self._lib.pkv_pool_seq_len(self._h, seq))
+
+    def block_tables(self, seqs, width: int):
+        """(table int32 [len(seqs), width] with -1 padding, seq_lens int32)."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        table = np.empty((len(ids), width), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        _raise(self._lib.pkv_pool_block_tables(self._h, ids.ctypes.data, len(ids),
+                                               table.ctypes.data, width, lens.ctypes.data))
+        return table, lens

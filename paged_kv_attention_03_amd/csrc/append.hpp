@@ -43,4 +43,30 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p) {
     st16(p.v_pool + dst, ld16(p.v_new + src));
 }
 
+// Whole-page copies inside the pool (K and V, every kv head): the private
+// copy a sequence takes of a shared page before writing into it.  One thread
+// moves one 16-byte chunk of the K page and the same chunk of the V page;
+// pairs naming a page outside the pool are skipped.
+struct CopyBlocksParams {
+    uint8_t* k_pool;
+    uint8_t* v_pool;
+    const int32_t* src;
+    const int32_t* dst;
+    int64_t num_pairs;
+    int64_t chunks_per_block;  // num_kv_heads * block_size * head_dim * elem_bytes / 16
+    int64_t num_blocks;
+};
+
+__global__ void __launch_bounds__(256) copy_blocks_kernel(CopyBlocksParams p) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = gid / p.chunks_per_block;
+    if (i >= p.num_pairs) return;
+    const int64_t c = gid - i * p.chunks_per_block;
+    const int64_t s = p.src[i], d = p.dst[i];
+    if (s < 0 || s >= p.num_blocks || d < 0 || d >= p.num_blocks) return;
+    const int64_t bb = p.chunks_per_block * 16;
+    st16(p.k_pool + d * bb + c * 16, ld16(p.k_pool + s * bb + c * 16));
+    st16(p.v_pool + d * bb + c * 16, ld16(p.v_pool + s * bb + c * 16));
+}
+
 }  // namespace pkv

@@ -20,6 +20,11 @@
 #include "append.hpp"
 #include "decode.hpp"
 #include "prefill.hpp"
+#include "pool.hpp"
+
+struct pkv_pool {
+    pkv::PagePool pool;
+};
 
 namespace {
 
@@ -411,6 +416,149 @@ int pkv_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int block_s
     for (size_t i = 1; i < seen.size(); ++i)
         if (seen[i] == seen[i - 1])
             return fail(PKV_E_METADATA, "slot %lld is written twice", (long long)seen[i]);
+    return ok();
+}
+
+
+// ---------------------------------------------------------------- pool manager
+
+pkv_pool_t* pkv_pool_create(int64_t num_blocks, int block_size, int max_seqs,
+                            int max_blocks_per_seq) {
+    if (num_blocks <= 0 || num_blocks > 0x7fffffffLL || block_size <= 0 || max_seqs <= 0 ||
+        max_blocks_per_seq <= 0) {
+        fail(PKV_E_ARG, "invalid pool sizes");
+        return nullptr;
+    }
+    try {
+        pkv_pool_t* p = new pkv_pool_t{pkv::PagePool(num_blocks, block_size, max_seqs,
+                                                     max_blocks_per_seq)};
+        ok();
+        return p;
+    } catch (...) {
+        fail(PKV_E_ARG, "host allocation of the pool tables failed");
+        return nullptr;
+    }
+}
+
+void pkv_pool_destroy(pkv_pool_t* pool) { delete pool; }
+
+int64_t pkv_pool_free_blocks(const pkv_pool_t* pool) {
+    return pool ? pool->pool.free_blocks() : -1;
+}
+
+int pkv_pool_can_admit(const pkv_pool_t* pool, int64_t num_tokens) {
+    return pool ? (pool->pool.can_admit(num_tokens) ? 1 : 0) : -1;
+}
+
+static int pool_status(pkv::PagePool::Status st, const char* what) {
+    switch (st) {
+    case pkv::PagePool::kOk: return ok();
+    case pkv::PagePool::kNoMem: return fail(PKV_E_NOMEM, "%s: too few free pages", what);
+    default: return fail(PKV_E_ARG, "%s: invalid sequence or size", what);
+    }
+}
+
+int pkv_pool_add_seq(pkv_pool_t* pool, int seq) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    return pool_status(pool->pool.add_seq(seq), "pkv_pool_add_seq");
+}
+
+int pkv_pool_fork(pkv_pool_t* pool, int parent, int child, int64_t shared_tokens) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    return pool_status(pool->pool.fork(parent, child, shared_tokens), "pkv_pool_fork");
+}
+
+int pkv_pool_append(pkv_pool_t* pool, int seq, int64_t num_tokens, int64_t* slots,
+                    int32_t* cow_src, int32_t* cow_dst, int* num_cow) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    if (num_tokens > 0 && !slots) return fail(PKV_E_ARG, "null slots");
+    pkv::PagePool& pp = pool->pool;
+    if (pp.live(seq) && num_tokens > 0 && pp.length(seq) % pp.block_size() != 0 &&
+        pp.refcount(pp.pages(seq).back()) > 1 && (!cow_src || !cow_dst || !num_cow))
+        return fail(PKV_E_ARG, "pkv_pool_append: a page copy is needed but cow outputs are NULL");
+    return pool_status(pp.append(seq, num_tokens, slots, cow_src, cow_dst, num_cow),
+                       "pkv_pool_append");
+}
+
+int pkv_pool_append_batch(pkv_pool_t* pool, const int* seqs, const int64_t* counts,
+                          int num_seqs, int64_t* slots, int32_t* cow_src, int32_t* cow_dst,
+                          int* num_cow) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    if (num_seqs < 0) return fail(PKV_E_ARG, "num_seqs %d < 0", num_seqs);
+    if (num_seqs == 0) {
+        if (num_cow) *num_cow = 0;
+        return ok();
+    }
+    if (!seqs || !counts || !slots || !cow_src || !cow_dst || !num_cow)
+        return fail(PKV_E_ARG, "null pointer argument");
+    return pool_status(pool->pool.append_batch(seqs, counts, num_seqs, slots, cow_src, cow_dst,
+                                               num_cow),
+                       "pkv_pool_append_batch");
+}
+
+int pkv_pool_truncate(pkv_pool_t* pool, int seq, int64_t new_len) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    return pool_status(pool->pool.truncate(seq, new_len), "pkv_pool_truncate");
+}
+
+int pkv_pool_free_seq(pkv_pool_t* pool, int seq) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    return pool_status(pool->pool.free_seq(seq), "pkv_pool_free_seq");
+}
+
+int64_t pkv_pool_seq_len(const pkv_pool_t* pool, int seq) {
+    return pool ? pool->pool.length(seq) : -1;
+}
+
+int pkv_pool_block_tables(const pkv_pool_t* pool, const int* seqs, int num_seqs, int32_t* table,
+                          int width, int32_t* seq_lens) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    if (num_seqs < 0 || width <= 0) return fail(PKV_E_ARG, "invalid sizes");
+    if (num_seqs == 0) return ok();
+    if (!seqs || !table) return fail(PKV_E_ARG, "null pointer argument");
+    const pkv::PagePool& pp = pool->pool;
+    for (int i = 0; i < num_seqs; ++i) {
+        if (!pp.live(seqs[i])) return fail(PKV_E_ARG, "sequence %d is not live", seqs[i]);
+        if ((int64_t)pp.pages(seqs[i]).size() > width)
+            return fail(PKV_E_ARG, "sequence %d holds %zu pages, table width %d", seqs[i],
+                        pp.pages(seqs[i]).size(), width);
+    }
+    for (int i = 0; i < num_seqs; ++i) {
+        const std::vector<int32_t>& pg = pp.pages(seqs[i]);
+        int32_t* row = table + (int64_t)i * width;
+        for (int j = 0; j < width; ++j) row[j] = j < (int)pg.size() ? pg[(size_t)j] : -1;
+        if (seq_lens) seq_lens[i] = (int32_t)pp.length(seqs[i]);
+    }
+    return ok();
+}
+
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                    int64_t num_pairs, int num_kv_heads, int head_dim, int block_size,
+                    int64_t num_blocks, pkv_dtype_t dtype, void* stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16)
+        return fail(PKV_E_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    if (num_pairs < 0) return fail(PKV_E_ARG, "num_pairs %lld < 0", (long long)num_pairs);
+    if (num_kv_heads <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PKV_E_ARG, "invalid sizes");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_E_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+    if (num_pairs == 0) return ok();
+    if (!k_pool || !v_pool || !src || !dst) return fail(PKV_E_ARG, "null pointer argument");
+    if (!aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKV_E_ARG, "pools must be 16-byte aligned");
+    pkv::CopyBlocksParams cp;
+    cp.k_pool = static_cast<uint8_t*>(k_pool);
+    cp.v_pool = static_cast<uint8_t*>(v_pool);
+    cp.src = src;
+    cp.dst = dst;
+    cp.num_pairs = num_pairs;
+    cp.chunks_per_block = (int64_t)num_kv_heads * block_size * head_dim * (int64_t)elem_bytes(dtype) / 16;
+    cp.num_blocks = num_blocks;
+    const int64_t grid = (num_pairs * cp.chunks_per_block + 255) / 256;
+    if (grid > 0x7fffffffLL) return fail(PKV_E_ARG, "too many pages for one launch");
+    hipLaunchKernelGGL(pkv::copy_blocks_kernel, dim3((unsigned)grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), cp);
+    if (int rc = hip_status("copy launch")) return rc;
     return ok();
 }
 

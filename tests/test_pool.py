@@ -1,0 +1,277 @@
+"""Host-side pool manager (pkv_pool_*), CPU only.
+
+Pinned two ways.  (1) Against an independent model of the bookkeeping written
+here (pages per sequence, reference counts, a free count) over long random
+operation sequences: slots, copy-on-write requests, free pages, block tables
+and lengths must agree after every operation, and a refused operation
+(too few pages) must change nothing.  (2) At the data level: every slot write
+stores a token id in a host array standing in for the pool, every requested
+page copy is carried out, and each live sequence read back through its block
+table must equal the token history it was built from (its shared prefix plus
+its own tokens) -- a missing or misplaced copy-on-write shows up as a sibling
+seeing another sequence's tokens.  Invariants from the pages: the pool never
+grows (free + held pages = num_blocks), a page a sequence writes into is held
+by that sequence alone, admission is exactly "the pages fit".
+"""
+import numpy as np
+import pytest
+
+import paged_kv_attention_03_amd as pkv
+
+
+class Model:
+    """Independent reference of the manager's semantics."""
+
+    def __init__(self, nb, bs, max_seqs, width):
+        self.nb, self.bs, self.max_seqs, self.width = nb, bs, max_seqs, width
+        self.seqs = {}          # seq -> [len, pages]
+        self.ref = {}           # page -> holders
+
+    def free(self):
+        return self.nb - len(self.ref)
+
+    def pages_for(self, n):
+        return -(-n // self.bs)
+
+
+def _check_same(pool, model):
+    assert pool.free_blocks == model.free()
+    for s in range(model.max_seqs):
+        if s in model.seqs:
+            n, pages = model.seqs[s]
+            assert pool.seq_len(s) == n
+            table, lens = pool.block_tables([s], model.width)
+            assert lens[0] == n
+            assert list(table[0][:len(pages)]) == pages
+            assert (table[0][len(pages):] == -1).all()
+        else:
+            assert pool.seq_len(s) == -1
+    # reference counts: each held page counted once per holder
+    holders = {}
+    for n, pages in model.seqs.values():
+        for p in pages:
+            holders[p] = holders.get(p, 0) + 1
+    assert holders == model.ref
+
+
+def _run_ops(seed, nb=40, bs=4, max_seqs=6, width=12, steps=400, data=False):
+    rng = np.random.default_rng(seed)
+    pool = pkv.PagePool(nb, bs, max_seqs, width)
+    model = Model(nb, bs, max_seqs, width)
+    store = np.full(nb * bs, -1, dtype=np.int64)   # token id held by each slot
+    hist = {}                                       # seq -> token ids
+    next_tok = 0
+    for _ in range(steps):
+        op = rng.integers(0, 5)
+        s = int(rng.integers(0, max_seqs))
+        if op == 0:                                   # add
+            if s in model.seqs:
+                with pytest.raises(pkv.PkvError):
+                    pool.add_seq(s)
+            else:
+                pool.add_seq(s)
+                model.seqs[s] = [0, []]
+                hist[s] = []
+        elif op == 1 and model.seqs:                  # fork from a live parent
+            par = int(rng.choice(list(model.seqs)))
+            if s in model.seqs:
+                continue
+            shared = int(rng.integers(0, model.seqs[par][0] + 1))
+            pool.fork(par, s, shared)
+            pages = model.seqs[par][1][:model.pages_for(shared)]
+            model.seqs[s] = [shared, list(pages)]
+            for p in pages:
+                model.ref[p] += 1
+            hist[s] = hist[par][:shared]
+        elif op == 2 and s in model.seqs:             # append n tokens
+            n = int(rng.integers(0, 7))
+            ln, pages = model.seqs[s]
+            need = model.pages_for(ln + n)
+            cow = n > 0 and ln % bs != 0 and model.ref[pages[-1]] > 1
+            fresh = need - len(pages) + (1 if cow else 0)
+            if need > width:
+                with pytest.raises(pkv.PkvError):
+                    pool.append(s, n)
+            elif fresh > model.free():
+                with pytest.raises(pkv.PkvError) as e:
+                    pool.append(s, n)
+                assert e.value.code == pkv.PKV_E_NOMEM
+            else:
+                slots, copies = pool.append(s, n)
+                if cow:
+                    assert len(copies) == 1 and copies[0][0] == pages[-1]
+                    src, dst = copies[0]
+                    assert dst not in model.ref
+                    model.ref[src] -= 1
+                    model.ref[dst] = 1
+                    pages[-1] = dst
+                    store[dst * bs:(dst + 1) * bs] = store[src * bs:(src + 1) * bs]
+                else:
+                    assert copies == []
+                while len(pages) < need:
+                    slot_page = None
+                    # the manager picks any free page: take it from the slots it returned
+                    for sl in slots:
+                        p = int(sl) // bs
+                        if p not in pages and p not in model.ref:
+                            slot_page = p
+                            break
+                    assert slot_page is not None
+                    pages.append(slot_page)
+                    model.ref[slot_page] = 1
+                model.seqs[s][0] = ln + n
+                exp = [pages[(ln + i) // bs] * bs + (ln + i) % bs for i in range(n)]
+                assert list(slots) == exp
+                for sl in slots:                      # the writer holds the page alone
+                    assert model.ref[int(sl) // bs] == 1
+                for i, sl in enumerate(slots):
+                    store[sl] = next_tok + i
+                hist[s] = hist[s] + [next_tok + i for i in range(n)]
+                next_tok += n
+        elif op == 3 and s in model.seqs:             # truncate
+            ln, pages = model.seqs[s]
+            nl = int(rng.integers(0, ln + 1))
+            pool.truncate(s, nl)
+            keep = model.pages_for(nl)
+            for p in pages[keep:]:
+                model.ref[p] -= 1
+                if model.ref[p] == 0:
+                    del model.ref[p]
+            model.seqs[s] = [nl, pages[:keep]]
+            hist[s] = hist[s][:nl]
+        elif op == 4 and s in model.seqs and rng.random() < 0.3:   # free
+            pool.free_seq(s)
+            for p in model.seqs[s][1]:
+                model.ref[p] -= 1
+                if model.ref[p] == 0:
+                    del model.ref[p]
+            del model.seqs[s]
+            del hist[s]
+        _check_same(pool, model)
+        assert pool.free_blocks + len(model.ref) == nb
+        if data:
+            for s2, (ln, pages) in model.seqs.items():
+                got = [int(store[pages[j // bs] * bs + j % bs]) for j in range(ln)]
+                assert got == hist[s2], f"sequence {s2} reads {got}, built {hist[s2]}"
+    pool.close()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bookkeeping_matches_model(seed):
+    _run_ops(seed)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_every_sequence_reads_its_own_history(seed):
+    _run_ops(100 + seed, nb=24, bs=3, max_seqs=5, width=10, steps=500, data=True)
+
+
+def test_admission_is_exactly_the_free_pages():
+    pool = pkv.PagePool(10, 16, 4, 100)
+    assert pool.can_admit(160) and not pool.can_admit(161)
+    pool.add_seq(0)
+    pool.append(0, 17)                   # two pages
+    assert pool.free_blocks == 8
+    assert pool.can_admit(128) and not pool.can_admit(129)
+    pool.add_seq(1)
+    with pytest.raises(pkv.PkvError) as e:
+        pool.append(1, 129)
+    assert e.value.code == pkv.PKV_E_NOMEM
+    assert pool.free_blocks == 8 and pool.seq_len(1) == 0   # nothing changed
+    pool.free_seq(0)
+    assert pool.free_blocks == 10
+
+
+def test_shared_prefix_pages_are_never_written():
+    """A 500-token prefix forked 16 ways (the agent fan-out): the full prefix
+    pages are shared by all, the partly filled last one is copied once per
+    writer, and every slot handed out lies in a page its writer holds alone."""
+    bs = 16
+    pool = pkv.PagePool(400, bs, 17, 64)
+    pool.add_seq(0)
+    pool.append(0, 500)
+    table0, _ = pool.block_tables([0], 64)
+    shared_pages = set(table0[0][:500 // bs].tolist())
+    last = int(table0[0][500 // bs])
+    copies = 0
+    for c in range(1, 17):
+        pool.fork(0, c, 500)
+    for step in range(5):
+        for c in range(1, 17):
+            slots, cp = pool.append(c, 1)
+            copies += len(cp)
+            if cp:
+                assert cp[0][0] == last
+            assert int(slots[0]) // bs not in shared_pages
+    assert copies == 16
+    tabs, lens = pool.block_tables(list(range(1, 17)), 64)
+    assert (lens == 505).all()
+    assert all(set(t[:500 // bs].tolist()) == shared_pages for t in tabs)
+    all_slots = []
+    for c in range(1, 17):
+        s, _ = pool.append(c, 3)
+        all_slots.extend(s.tolist())
+    assert len(set(all_slots)) == len(all_slots)
+
+
+def test_invalid_calls_are_rejected():
+    with pytest.raises(pkv.PkvError):
+        pkv.PagePool(0, 16, 4, 4)
+    pool = pkv.PagePool(8, 16, 2, 4)
+    with pytest.raises(pkv.PkvError):
+        pool.add_seq(2)                  # out of range
+    pool.add_seq(0)
+    with pytest.raises(pkv.PkvError):
+        pool.fork(0, 0, 0)               # child live
+    with pytest.raises(pkv.PkvError):
+        pool.fork(0, 1, 1)               # more than the parent holds
+    with pytest.raises(pkv.PkvError):
+        pool.append(0, 65)               # past max_blocks_per_seq
+    with pytest.raises(pkv.PkvError):
+        pool.truncate(0, 1)              # longer than the sequence
+    with pytest.raises(pkv.PkvError):
+        pool.free_seq(1)                 # not live
+    with pytest.raises(pkv.PkvError):
+        pool.block_tables([1], 4)
+
+
+def test_batch_append_equals_one_call_per_sequence():
+    a = pkv.PagePool(200, 16, 8, 40)
+    b = pkv.PagePool(200, 16, 8, 40)
+    for p in (a, b):
+        p.add_seq(0)
+        p.append(0, 37)
+        for c in range(1, 6):
+            p.fork(0, c, 37 if c % 2 else 32)
+    rng = np.random.default_rng(3)
+    for step in range(20):
+        seqs = [int(x) for x in rng.permutation(6)[:4]]
+        counts = [int(x) for x in rng.integers(0, 5, size=4)]
+        sa, ca = a.append_batch(seqs, counts)
+        sb, cb = [], []
+        for s, n in zip(seqs, counts):
+            x, c = b.append(s, n)
+            sb.extend(x.tolist())
+            cb.extend(c)
+        assert sa.tolist() == sb and ca == cb
+        assert a.block_tables(range(6), 40)[0].tolist() == b.block_tables(range(6), 40)[0].tolist()
+
+
+def test_batch_append_is_all_or_nothing():
+    pool = pkv.PagePool(6, 16, 4, 10)
+    for s in range(3):
+        pool.add_seq(s)
+    pool.append(0, 16)
+    before = (pool.free_blocks, pool.block_tables([0, 1, 2], 10))
+    with pytest.raises(pkv.PkvError) as e:
+        pool.append_batch([1, 2], [48, 48])          # 6 pages wanted, 5 free
+    assert e.value.code == pkv.PKV_E_NOMEM
+    with pytest.raises(pkv.PkvError):
+        pool.append_batch([1, 1], [1, 1])            # listed twice
+    with pytest.raises(pkv.PkvError):
+        pool.append_batch([1, 3], [1, 1])            # 3 is not live
+    after = (pool.free_blocks, pool.block_tables([0, 1, 2], 10))
+    assert before[0] == after[0]
+    assert before[1][0].tolist() == after[1][0].tolist()
+    slots, _ = pool.append_batch([2, 1], [3, 2])
+    assert pool.seq_len(1) == 2 and pool.seq_len(2) == 3 and len(slots) == 5
