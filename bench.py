@@ -101,7 +101,7 @@ class Step:
 def time_steps(step: Step, steps: int, warmup: int, flush_bytes: int = 0):
     """Whole-step wall time over ``steps`` steps, and the attention call's
     average duration from HIP events recorded on the launch stream."""
-    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    flush = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda") if flush_bytes else None
     for _ in range(warmup):
         step.append()
         step.attention()
@@ -118,12 +118,14 @@ def time_steps(step: Step, steps: int, warmup: int, flush_bytes: int = 0):
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
     else:
-        # caches are cleared before every step; the wall time then excludes the
+        # caches are cleared before every step by reading a buffer larger than
+        # L2 + Infinity Cache (a read leaves no dirty lines whose write-back
+        # would be charged to the step); the wall time then excludes the
         # clearing by summing per-step event pairs around append + attention
         wall_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(steps)]
         for (a, b), (c, d) in zip(ev, wall_ev):
-            flush.fill_(1)
+            sink = flush.sum()  # noqa: F841
             c.record()
             step.append()
             a.record()
