@@ -52,6 +52,13 @@ constexpr int kMaxDecodeSeqs = 16384;  // sequences the plan kernel can hold in 
 constexpr int kWindowPages = 256;      // block-table entries staged per window
 constexpr int kInlinePlanSeqs = 512;   // up to this many sequences each decode wave
                                        // plans its own pieces (no plan kernel)
+// Steps whose decode K/V exceed this many bytes (twice the 256 MB Infinity
+// Cache) stream them with non-temporal loads: read once, they would only
+// displace each other from the caches, and the hint lifts the read rate of a
+// pure stream by ~10% on MI355X (measured: 7.0 against 6.4 TB/s).  Smaller
+// steps keep cacheable loads, which let repeated pages (a shared prefix, the
+// next step's contexts) hit the Infinity Cache.
+constexpr int64_t kStreamBytes = 512ll << 20;
 
 // A wave's piece of one (sequence, kv head) segment: page pairs [pi0, pi1).
 struct Portion {
@@ -273,6 +280,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     const int S = p.num_seqs;
     int pb = 0, pe = 0;       // plan-kernel mode: this wave's pieces
     int64_t u0 = 0, u1 = 0;   // inline mode: this wave's units [u0, u1)
+    int64_t units = 0;        // (sequence, kv head, page pair) units of the step
     if (inl) {
         // page pairs of every sequence and their exclusive prefix, in LDS
         const int per = (S + kWave - 1) / kWave;
@@ -304,11 +312,15 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
         u0 = wave_start(w, U);
         u1 = wave_start(w + 1, U);
         if (u0 >= u1) return;
+        units = U;
     } else {
         pb = p.portion_begin[w];
         pe = p.portion_begin[w + 1];
         if (pb >= pe) return;
+        units = (int64_t)p.Hkv * p.pair_prefix[S];
     }
+    // a unit is one page pair of one kv head: K and V of two pages
+    const bool stream_nt = units * 4 * kPage * Gm::RB > kStreamBytes;
     auto pref = [&](int s) { return __builtin_amdgcn_readfirstlane(lds_pref[s]); };
     // inline mode: the walk over the segments that meet [u0, u1) -- sequence
     // ws, kv head wg, ws's pairs wc, pieces emitted so far
@@ -419,18 +431,25 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                 wseq = is;
             }
             const int64_t head_off = (int64_t)ig * kPage * Gm::RB;
+            // the same loads in both arms (same registers): only the cache hint differs
+            auto load_pair = [&](auto nt_tag) {
+                constexpr bool NT = decltype(nt_tag)::value;
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int pg = x ? pb2 : pa;
-                const int64_t blk = __builtin_amdgcn_readfirstlane(lds_bid[pg - wstart]);
-                const uint8_t* kb = kpool + blk * page_stride + head_off;
-                const uint8_t* vb = vpool + blk * page_stride + head_off;
+                for (int x = 0; x < 2; ++x) {
+                    const int pg = x ? pb2 : pa;
+                    const int64_t blk = __builtin_amdgcn_readfirstlane(lds_bid[pg - wstart]);
+                    const auto kr = buffer_rsrc(kpool + blk * page_stride + head_off, kPage * Gm::RB);
+                    const auto vr = buffer_rsrc(vpool + blk * page_stride + head_off, kPage * Gm::RB);
 #pragma unroll
-                for (int i = 0; i < Gm::KCH; ++i)
-                    R.k[x][i] = ld16(kb + col * Gm::RB + i * 64 + grp * 16);
+                    for (int i = 0; i < Gm::KCH; ++i)
+                        R.k[x][i] = buffer_ld16<NT>(kr, col * Gm::RB + i * 64 + grp * 16);
 #pragma unroll
-                for (int c = 0; c < Gm::VCH; ++c) R.v[x][c] = ld16(vb + (c * kWave + lane) * 16);
-            }
+                    for (int c = 0; c < Gm::VCH; ++c)
+                        R.v[x][c] = buffer_ld16<NT>(vr, (c * kWave + lane) * 16);
+                }
+            };
+            if (stream_nt) load_pair(std::true_type{});
+            else load_pair(std::false_type{});
             // advance; past the end the last pair is loaded again (cache hit, unused)
             if (!idone && ++ipi == iend) {
                 if (ip + 1 < n) {

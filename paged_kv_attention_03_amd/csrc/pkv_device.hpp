@@ -53,6 +53,22 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Buffer resource over `bytes` bytes from base (raw, stride 0; loads past
+// the end read zero).  Word 3 selects the 32-bit data format that untyped
+// buffer loads on CDNA expect.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16-byte buffer load at byte offset off; NT sets the non-temporal hint (the
+// data is streamed past the caches instead of displacing reused lines).  The
+// hint is an immediate of the instruction, so code that picks it at run time
+// keeps two loads the compiler cannot merge.
+template <bool NT>
+__device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
