@@ -431,15 +431,20 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                 wseq = is;
             }
             const int64_t head_off = (int64_t)ig * kPage * Gm::RB;
-            // the same loads in both arms (same registers): only the cache hint differs
+            // The same loads in both arms (same registers): only the cache hint
+            // differs.  A pair issued past the cursor's end (never consumed) and
+            // the second page of a pair that has one page in range use empty
+            // resources: the loads return zeros without touching memory, which
+            // matters once they are not cache hits.
             auto load_pair = [&](auto nt_tag) {
                 constexpr bool NT = decltype(nt_tag)::value;
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int pg = x ? pb2 : pa;
                     const int64_t blk = __builtin_amdgcn_readfirstlane(lds_bid[pg - wstart]);
-                    const auto kr = buffer_rsrc(kpool + blk * page_stride + head_off, kPage * Gm::RB);
-                    const auto vr = buffer_rsrc(vpool + blk * page_stride + head_off, kPage * Gm::RB);
+                    const int bytes = (idone || (x && pb2 == pa)) ? 0 : kPage * Gm::RB;
+                    const auto kr = buffer_rsrc(kpool + blk * page_stride + head_off, bytes);
+                    const auto vr = buffer_rsrc(vpool + blk * page_stride + head_off, bytes);
 #pragma unroll
                     for (int i = 0; i < Gm::KCH; ++i)
                         R.k[x][i] = buffer_ld16<NT>(kr, col * Gm::RB + i * 64 + grp * 16);
@@ -450,7 +455,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
             };
             if (stream_nt) load_pair(std::true_type{});
             else load_pair(std::false_type{});
-            // advance; past the end the last pair is loaded again (cache hit, unused)
+            // advance; past the end the last pair is issued again (zeros, unused)
             if (!idone && ++ipi == iend) {
                 if (ip + 1 < n) {
                     ++ip;
