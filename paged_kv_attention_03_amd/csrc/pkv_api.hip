@@ -144,7 +144,11 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
     if (max_seqlen_q > pl.wmax) {  // longer sequences: chunked prefill
         const long tiles = (total_q + pp.tile_tokens - 1) / pp.tile_tokens + num_seqs;
         // a tile's pages: at most ceil(max_seqlen_k / 16) + 1, rounded up to pairs
-        const bool long_ctx = ((long)pp.max_seqlen_k + kBlock - 1) / kBlock + 2 > pkv::kPrefillIdTable;
+        // (or a pool whose (page, kv head) offsets / 256 exceed 32 bits)
+        const bool long_ctx =
+            ((long)pp.max_seqlen_k + kBlock - 1) / kBlock + 2 > pkv::kPrefillIdTable ||
+            (uint64_t)pp.num_blocks * (uint64_t)pp.Hkv * (pkv::PrefillGeom<T, D>::PAGE / 256) >
+                0xffffffffull;
         if (long_ctx)
             hipLaunchKernelGGL((pkv::prefill_kernel<T, D, true>), dim3((unsigned)(tiles * pp.Hkv)),
                                dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);

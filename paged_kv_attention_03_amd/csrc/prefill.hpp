@@ -74,10 +74,22 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // the kernel orders these transfers itself, with explicit vmcnt waits and a
 // workgroup barrier before a staged buffer is read.
 __device__ __forceinline__ void load_to_lds16(const void* g, uint8_t* block) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_t*)block;
+    // block is wave-uniform; made scalar explicitly, as M0 takes a scalar register
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)block);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(m0), "v"(g)
+                 : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (the global address is base + off): no per-lane
+// 64-bit address arithmetic.
+__device__ __forceinline__ void load_to_lds16(const uint8_t* base, uint32_t off, uint8_t* block) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)block);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(off), "s"(base)
                  : "memory", "m0");
 }
 
@@ -197,7 +209,8 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     constexpr int SPLIT = Gm::SPLIT;
     constexpr int NW = Gm::NW;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * Gm::STAGE];
-    __shared__ __attribute__((aligned(8))) int32_t lds_bid[LONG ? 2 : kPrefillIdTable];
+    // !LONG: byte offset / 256 of each staged (page, kv head) inside a pool
+    __shared__ __attribute__((aligned(8))) uint32_t lds_bid[LONG ? 2 : kPrefillIdTable];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -288,46 +301,68 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         src_off[c] = row * Gm::RB + (kbuf ? swz_k<Gm::CPR>(row, lane % Gm::CPR)
                                           : swz_v<Gm::CPR>(row, lane % Gm::CPR)) * 16;
     }
-    // Block ids of stage st's two pages (an odd page count repeats the last
-    // page; ids outside the pool read page 0), fetched a round ahead of their
-    // use.  Up to 64K keys the workgroup stages its block-table entries in
-    // LDS once; beyond that (LONG) they are read through the scalar data cache
-    // (constant address space: the table is read-only and the index uniform),
-    // which is counted apart from the global->LDS transfers but shares the
-    // LDS counter, so it is slightly slower.
+    // What stage st's transfers need from the block table (an odd page
+    // count repeats the last page; ids outside the pool read page 0), fetched
+    // a round ahead of their use.  Up to 64K keys the workgroup stages, once,
+    // the byte offset / 256 of every (page, kv head) it reads in LDS (clamped
+    // and scaled there, so a transfer only shifts and adds); every load of a
+    // wavefront then reads the same one of a stage's two pages (kOnePage) or
+    // picks per load.  Beyond that (LONG) the block ids are read through the
+    // scalar data cache (constant address space: the table is read-only and
+    // the index uniform), which is counted apart from the global->LDS
+    // transfers but shares the LDS counter, so it is slightly slower.
+    constexpr bool kOnePage = NW % (2 * BPP) == 0;
+    const int pw = (wave / BPP) & 1;  // kOnePage: the page this wavefront loads
     typedef __attribute__((address_space(4))) const int32_t cint32_t;
     const cint32_t* bt_row =
         (const cint32_t*)(p.block_tables + (int64_t)s * p.max_blocks + first_page);
     if constexpr (!LONG) {
-        for (int i = tid; i < 2 * nstage; i += blockDim.x)
-            lds_bid[i] = p.block_tables[(int64_t)s * p.max_blocks + first_page + min(i, npages - 1)];
+        for (int i = tid; i < 2 * nstage; i += blockDim.x) {
+            const int id = p.block_tables[(int64_t)s * p.max_blocks + first_page + min(i, npages - 1)];
+            const int64_t b = (id >= 0 && id < p.num_blocks) ? id : 0;
+            lds_bid[i] = (uint32_t)((b * p.Hkv + g) * (Gm::PAGE / 256));
+        }
         __syncthreads();
     }
     auto stage_ids = [&](int st) {
         if constexpr (LONG) {
             return int2{bt_row[2 * st], bt_row[min(2 * st + 1, npages - 1)]};
+        } else if constexpr (kOnePage) {
+            // wave-uniform: made scalar at once
+            const int v = __builtin_amdgcn_readfirstlane((int)lds_bid[2 * st + pw]);
+            return int2{v, v};
         } else {
-            return *reinterpret_cast<const int2*>(&lds_bid[2 * st]);
+            const uint2 o = *reinterpret_cast<const uint2*>(&lds_bid[2 * st]);
+            return int2{__builtin_amdgcn_readfirstlane((int)o.x),
+                        __builtin_amdgcn_readfirstlane((int)o.y)};
         }
     };
     auto issue_stage = [&](int st, int2 ids) {
-        // wave-uniform ids (LDS values are made scalar), so the page
-        // addresses are computed on the scalar unit
-        const int ia = LONG ? ids.x : __builtin_amdgcn_readfirstlane(ids.x);
-        const int ib = LONG ? ids.y : __builtin_amdgcn_readfirstlane(ids.y);
-        const int64_t ba = (ia >= 0 && ia < p.num_blocks) ? ia : 0;
-        const int64_t bb = (ib >= 0 && ib < p.num_blocks) ? ib : 0;
-        const uint8_t* kA = kpool + ba * page_stride + head_off;
-        const uint8_t* kB = kpool + bb * page_stride + head_off;
-        const uint8_t* vA = vpool + ba * page_stride + head_off;
-        const uint8_t* vB = vpool + bb * page_stride + head_off;
         uint8_t* base = lds + (st % NS) * Gm::STAGE;
+        if constexpr (LONG) {
+            const int64_t ba = (ids.x >= 0 && ids.x < p.num_blocks) ? ids.x : 0;
+            const int64_t bb = (ids.y >= 0 && ids.y < p.num_blocks) ? ids.y : 0;
+            const uint8_t* kA = kpool + ba * page_stride + head_off;
+            const uint8_t* kB = kpool + bb * page_stride + head_off;
+            const uint8_t* vA = vpool + ba * page_stride + head_off;
+            const uint8_t* vB = vpool + bb * page_stride + head_off;
 #pragma unroll
-        for (int c = 0; c < Gm::LPT; ++c) {
-            const int blk = c * NW + wave;
-            const int buf = blk / BPP;                 // 0 K a, 1 K b, 2 V a, 3 V b
-            const uint8_t* src = buf == 0 ? kA : buf == 1 ? kB : buf == 2 ? vA : vB;
-            load_to_lds16(src + src_off[c], base + blk * 1024);
+            for (int c = 0; c < Gm::LPT; ++c) {
+                const int blk = c * NW + wave;
+                const int buf = blk / BPP;             // 0 K a, 1 K b, 2 V a, 3 V b
+                const uint8_t* src = buf == 0 ? kA : buf == 1 ? kB : buf == 2 ? vA : vB;
+                load_to_lds16(src + src_off[c], base + blk * 1024);
+            }
+        } else {
+            const uint64_t oa = (uint64_t)(uint32_t)ids.x << 8;
+            const uint64_t ob = (uint64_t)(uint32_t)ids.y << 8;
+#pragma unroll
+            for (int c = 0; c < Gm::LPT; ++c) {
+                const int blk = c * NW + wave;
+                const int buf = blk / BPP;             // 0 K a, 1 K b, 2 V a, 3 V b
+                const uint8_t* pool = (buf >> 1) ? vpool : kpool;
+                load_to_lds16(pool + ((buf & 1) ? ob : oa), (uint32_t)src_off[c], base + blk * 1024);
+            }
         }
     };
 
@@ -523,21 +558,33 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     // slots take the stages NS - SPLIT ahead.
     // ids[j]: block ids of the stage the next round loads as its j-th
     int2 ids[SPLIT];
+    // Interior rounds (EDGE false) also lie far enough from the end that
+    // every stage they wait for and issue exists: their wait is a constant and
+    // their transfers are unconditional.
     auto round = [&](auto edge_tag, auto slot_tag, int rr) {
-        const int last_needed = min(rr * SPLIT + SPLIT - 1, nstage - 1);
-        const int last_issued = min(rr * SPLIT + NS - SPLIT - 1, nstage - 1);
-        wait_stages<Gm::LPT, NS - 2 * SPLIT>(last_issued - last_needed);
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        if constexpr (EDGE) {
+            const int last_needed = min(rr * SPLIT + SPLIT - 1, nstage - 1);
+            const int last_issued = min(rr * SPLIT + NS - SPLIT - 1, nstage - 1);
+            wait_stages<Gm::LPT, NS - 2 * SPLIT>(last_issued - last_needed);
+        } else {
+            wait_vmcnt<(NS - 2 * SPLIT) * Gm::LPT>();
+        }
         barrier_keep_loads_in_flight();
 #pragma unroll
         for (int j = 0; j < SPLIT; ++j) {
             const int st = rr * SPLIT + NS - SPLIT + j;
-            if (st < nstage) issue_stage(st, ids[j]);
+            if (!EDGE || st < nstage) issue_stage(st, ids[j]);
         }
         if constexpr (!LONG) {
 #pragma unroll
             for (int j = 0; j < SPLIT; ++j) {
                 const int nx = rr * SPLIT + NS + j;
-                if (nx < nstage) ids[j] = stage_ids(nx);
+                if (EDGE) {
+                    if (nx < nstage) ids[j] = stage_ids(nx);
+                } else {
+                    ids[j] = stage_ids(min(nx, nstage - 1));  // used only if it exists
+                }
             }
         }
         const int st = rr * SPLIT + half;
@@ -573,7 +620,10 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     const int nround = (nstage + SPLIT - 1) / SPLIT;
     const int full = (pos_min - first_page * kPage - 2 * kPage + 1) < 0
                          ? 0 : (pos_min - first_page * kPage - 2 * kPage + 1) / (2 * kPage) + 1;
-    const int r_hi = min(nstage, full) / SPLIT;  // rounds [1, r_hi) are interior
+    // rounds [1, r_hi) are interior: every key of theirs lies in
+    // [kv_start, first position of the tile], and every stage they issue,
+    // up to rr * SPLIT + NS - 1, exists
+    const int r_hi = min(min(nstage, full) / SPLIT, nstage >= NS ? (nstage - NS) / SPLIT + 1 : 0);
     round(std::true_type{}, Dyn{}, 0);
     int rr = 1;
     for (; rr + U - 1 < r_hi; rr += U) {
