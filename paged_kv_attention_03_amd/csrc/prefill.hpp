@@ -83,10 +83,10 @@ __device__ __forceinline__ void load_to_lds16(const void* g, uint8_t* block) {
 }
 
 // The same with a wave-uniform 64-bit base in scalar registers and a 32-bit
-// per-lane byte offset (the global address is base + off): no per-lane
-// 64-bit address arithmetic.
-__device__ __forceinline__ void load_to_lds16(const uint8_t* base, uint32_t off, uint8_t* block) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)block);
+// per-lane byte offset (the global address is base + off), and the LDS block
+// given as an LDS byte address: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void load_to_lds16(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(m0), "v"(off), "s"(base)
@@ -209,8 +209,11 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     constexpr int SPLIT = Gm::SPLIT;
     constexpr int NW = Gm::NW;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * Gm::STAGE];
-    // !LONG: byte offset / 256 of each staged (page, kv head) inside a pool
-    __shared__ __attribute__((aligned(8))) uint32_t lds_bid[LONG ? 2 : kPrefillIdTable];
+    // !LONG: byte offset / 256 of each staged (page, kv head) inside a pool,
+    // page-major: [page of the stage (0, 1)][stage], each row padded so that
+    // reads a round past the last stage stay inside it
+    constexpr int kIdRow = kPrefillIdTable / 2 + 16;
+    __shared__ __attribute__((aligned(8))) uint32_t lds_bid[LONG ? 2 : 2 * kIdRow];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -320,7 +323,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         for (int i = tid; i < 2 * nstage; i += blockDim.x) {
             const int id = p.block_tables[(int64_t)s * p.max_blocks + first_page + min(i, npages - 1)];
             const int64_t b = (id >= 0 && id < p.num_blocks) ? id : 0;
-            lds_bid[i] = (uint32_t)((b * p.Hkv + g) * (Gm::PAGE / 256));
+            lds_bid[(i & 1) * kIdRow + (i >> 1)] = (uint32_t)((b * p.Hkv + g) * (Gm::PAGE / 256));
         }
         __syncthreads();
     }
@@ -329,16 +332,17 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             return int2{bt_row[2 * st], bt_row[min(2 * st + 1, npages - 1)]};
         } else if constexpr (kOnePage) {
             // wave-uniform: made scalar at once
-            const int v = __builtin_amdgcn_readfirstlane((int)lds_bid[2 * st + pw]);
+            const int v = __builtin_amdgcn_readfirstlane((int)lds_bid[pw * kIdRow + st]);
             return int2{v, v};
         } else {
-            const uint2 o = *reinterpret_cast<const uint2*>(&lds_bid[2 * st]);
-            return int2{__builtin_amdgcn_readfirstlane((int)o.x),
-                        __builtin_amdgcn_readfirstlane((int)o.y)};
+            return int2{__builtin_amdgcn_readfirstlane((int)lds_bid[st]),
+                        __builtin_amdgcn_readfirstlane((int)lds_bid[kIdRow + st])};
         }
     };
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)lds;  // LDS byte address of the ring
     auto issue_stage = [&](int st, int2 ids) {
         uint8_t* base = lds + (st % NS) * Gm::STAGE;
+        const uint32_t lbase = lds0 + (uint32_t)((st % NS) * Gm::STAGE);
         if constexpr (LONG) {
             const int64_t ba = (ids.x >= 0 && ids.x < p.num_blocks) ? ids.x : 0;
             const int64_t bb = (ids.y >= 0 && ids.y < p.num_blocks) ? ids.y : 0;
@@ -361,7 +365,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                 const int blk = c * NW + wave;
                 const int buf = blk / BPP;             // 0 K a, 1 K b, 2 V a, 3 V b
                 const uint8_t* pool = (buf >> 1) ? vpool : kpool;
-                load_to_lds16(pool + ((buf & 1) ? ob : oa), (uint32_t)src_off[c], base + blk * 1024);
+                load_to_lds16(pool + ((buf & 1) ? ob : oa), (uint32_t)src_off[c], lbase + blk * 1024);
             }
         }
     };
@@ -385,6 +389,9 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     for (int i = 0; i < Gm::KCH; ++i)
         koff[i] = hoff + col * Gm::RB + swz_k<Gm::CPR>(col, 4 * i + grp) * 16;
     int voff[Gm::NT];   // bf16 V^T: row 4grp + col/4, columns 16t + 4(col%4) .. +3
+    // (both also 64 KiB up, for slots past the 16-bit immediate offset of LDS
+    // reads; kept opaque so that they stay in registers)
+    int koff_hi[Gm::KCH], voff_hi[Gm::NT];
     {
         const int vrow = 4 * grp + (col >> 2);
         const int vsub = (col & 3) * 8;
@@ -392,6 +399,16 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         for (int t = 0; t < Gm::NT; ++t)
             voff[t] = hoff + vrow * Gm::RB + swz_v<Gm::CPR>(vrow, 2 * t + (vsub >> 4)) * 16 +
                       (vsub & 15);
+    }
+#pragma unroll
+    for (int i = 0; i < Gm::KCH; ++i) {
+        koff_hi[i] = koff[i] + 65536;
+        asm volatile("" : "+v"(koff_hi[i]));
+    }
+#pragma unroll
+    for (int t = 0; t < Gm::NT; ++t) {
+        voff_hi[t] = voff[t] + 65536;
+        asm volatile("" : "+v"(voff_hi[t]));
     }
 
     // One stage.  `slot_tag` is the compile-time ring slot of the round
@@ -404,7 +421,11 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     auto compute = [&](auto edge_tag, auto slot_tag, int dyn_slot, int st) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         constexpr int SLOT = decltype(slot_tag)::value;
-        const uint8_t* sb = lds + (SLOT >= 0 ? SLOT : dyn_slot) * Gm::STAGE;
+        // slots from 64 KiB on use the offsets 64 KiB up and a smaller base
+        constexpr bool HI = SLOT >= 0 && SLOT * Gm::STAGE >= 65536;
+        const uint8_t* sb = lds + (SLOT >= 0 ? SLOT : dyn_slot) * Gm::STAGE - (HI ? 65536 : 0);
+        const int* ko = HI ? koff_hi : koff;
+        const int* vo = HI ? voff_hi : voff;
         const int pa = first_page + 2 * st;
         // ---- operands from LDS: K for the logits, and (bfloat16) V^T for the
         // product, read up front so their latency overlaps the softmax
@@ -413,13 +434,13 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int i = 0; i < Gm::KCH; ++i)
-                kop[x][i] = *reinterpret_cast<const u32x4*>(sb + x * Gm::PAGE + koff[i]);
+                kop[x][i] = *reinterpret_cast<const u32x4*>(sb + x * Gm::PAGE + ko[i]);
         u32x4 vop[kBF ? Gm::NT : 1];
         if constexpr (kBF) {
 #pragma unroll
             for (int t = 0; t < Gm::NT; ++t) {
-                const uint2 lo = lds_read_tr16(sb + 2 * Gm::PAGE + voff[t]);
-                const uint2 hi = lds_read_tr16(sb + 3 * Gm::PAGE + voff[t]);
+                const uint2 lo = lds_read_tr16(sb + 2 * Gm::PAGE + vo[t]);
+                const uint2 hi = lds_read_tr16(sb + 3 * Gm::PAGE + vo[t]);
                 vop[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
             }
         }
@@ -540,7 +561,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                     for (int t = 0; t < Gm::NT; ++t) {
                         const int dcol = t * 16 + col;
                         float v = *reinterpret_cast<const float*>(
-                            sb + hoff + (2 + x) * Gm::PAGE + key * Gm::RB +
+                            sb + (HI ? 65536 : 0) + hoff + (2 + x) * Gm::PAGE + key * Gm::RB +
                             swz_v<Gm::CPR>(key, dcol >> 2) * 16 + (dcol & 3) * 4);
                         if constexpr (EDGE) v = kval[x * 4 + u] ? v : 0.f;
 #pragma unroll
@@ -582,9 +603,18 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                 const int nx = rr * SPLIT + NS + j;
                 if (EDGE) {
                     if (nx < nstage) ids[j] = stage_ids(nx);
-                } else {
-                    ids[j] = stage_ids(min(nx, nstage - 1));  // used only if it exists
+                } else if constexpr (!(kOnePage && SPLIT == 2)) {
+                    ids[j] = stage_ids(nx);  // inside the padded row; used only if it exists
                 }
+            }
+            if constexpr (!EDGE && kOnePage && SPLIT == 2) {
+                // both stages of the next round in one read (an even index)
+                const uint2 o =
+                    *reinterpret_cast<const uint2*>(&lds_bid[pw * kIdRow + rr * SPLIT + NS]);
+                const int a = __builtin_amdgcn_readfirstlane((int)o.x);
+                const int b = __builtin_amdgcn_readfirstlane((int)o.y);
+                ids[0] = int2{a, a};
+                ids[1] = int2{b, b};
             }
         }
         const int st = rr * SPLIT + half;
