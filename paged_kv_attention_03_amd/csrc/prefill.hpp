@@ -359,7 +359,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             }
         } else {
             const uint64_t oa = (uint64_t)(uint32_t)ids.x << 8;
-            const uint64_t ob = (uint64_t)(uint32_t)ids.y << 8;
+            const uint64_t ob = kOnePage ? oa : (uint64_t)(uint32_t)ids.y << 8;
 #pragma unroll
             for (int c = 0; c < Gm::LPT; ++c) {
                 const int blk = c * NW + wave;
@@ -370,6 +370,9 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         }
     };
 
+    // all-ones bf16 operand of the column-sum product, kept in registers
+    u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    asm volatile("" : "+v"(ones));
     f32x4 acc[2][Gm::NT];
     f32x4 lsum[2];  // column sums of P, accumulated on the matrix cores
 #pragma unroll
@@ -529,7 +532,6 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         mfma_priority(1);
         // ---- O^T += V^T P^T, and the column sums of P
         if constexpr (kBF) {
-            const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) lsum[nt] = mfma_bf16(ones, pb[nt], lsum[nt]);
             uint32_t keep[4];
