@@ -238,6 +238,14 @@ def extra_prefill(steps: int, warmup: int):
            "step_ms": wall * 1e3, "attention_ms": attn * 1e3}
     del sm
     torch.cuda.empty_cache()
+    res.update(prefill_chunks(steps, warmup))
+    return res
+
+
+def prefill_chunks(steps: int, warmup: int):
+    """The mixed workload's two 512-token chunks as a step of their own: the
+    prefill kernel alone against the dense bf16 matrix peak."""
+    mixed = W.config_step(3, poison=False)
     idx = [i for i, n in enumerate(mixed.q_lens) if n > 1]
     pre = W.build_step("mixed-prefill-chunks", [mixed.seq_lens[i] for i in idx],
                        [mixed.q_lens[i] for i in idx], 32, 8, 128, torch.bfloat16, 3000,
@@ -245,9 +253,9 @@ def extra_prefill(steps: int, warmup: int):
     sp = Step(pre, gen_device="cuda")
     _, pattn, pmed, _ = time_steps(sp, steps, warmup, flush_bytes=1 << 30)
     fl = prefill_flops(pre)
-    res.update({"prefill_gflop": fl / 1e9, "prefill_ms": pattn * 1e3,
-                "prefill_tflops": fl / pattn / 1e12,
-                "prefill_mfma_util": fl / pattn / 1e12 / BF16_DENSE_TFLOPS})
+    res = {"prefill_gflop": fl / 1e9, "prefill_ms": pattn * 1e3,
+           "prefill_tflops": fl / pattn / 1e12,
+           "prefill_mfma_util": fl / pattn / 1e12 / BF16_DENSE_TFLOPS}
     del sp
     torch.cuda.empty_cache()
     return res
@@ -313,6 +321,8 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the two prefill chunks of the mixed workload (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -322,6 +332,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.manual_seed(0)
+    if args.prefill_only:
+        print(json.dumps({"workload": "mixed-prefill-chunks", **prefill_chunks(args.steps, args.warmup)}),
+              flush=True)
+        return
     k = args.config
     if k == 4:
         run_main = bench_agent
