@@ -448,26 +448,36 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             }
         }
         mfma_priority(1);
-        // ---- S^T tiles: keys of page x as rows, this wavefront's rows as columns
+        // ---- S^T tiles: keys of page x as rows, this wavefront's rows as columns.
+        // The four tiles accumulate over the head dimension in four independent
+        // chains, issued step by step across the chains (a scheduling barrier
+        // after each step) so that a product never waits on the one just before
+        // it: a dependent product issues only ~52 cycles after its predecessor,
+        // four independent ones every 16.
         f32x4 sx[2][2];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (kBF) {
+            for (int nt = 0; nt < 2; ++nt) sx[nt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < Gm::KCH; ++i) sacc = mfma_bf16(kop[x][i], qop[nt][i], sacc);
-                } else {
+        for (int i = 0; i < Gm::KCH; ++i) {
+            if constexpr (kBF) {
 #pragma unroll
-                    for (int i = 0; i < Gm::KCH; ++i)
+                for (int x = 0; x < 2; ++x)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            sacc = mfma_f32(__uint_as_float(kop[x][i][t]),
-                                            __uint_as_float(qop[nt][i][t]), sacc);
-                }
-                sx[nt][x] = sacc;
+                    for (int nt = 0; nt < 2; ++nt)
+                        sx[nt][x] = mfma_bf16(kop[x][i], qop[nt][i], sx[nt][x]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt)
+                            sx[nt][x] = mfma_f32(__uint_as_float(kop[x][i][t]),
+                                                 __uint_as_float(qop[nt][i][t]), sx[nt][x]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         mfma_priority(0);
         bool kval[8];
