@@ -16,20 +16,23 @@
 // Keys are the MFMA rows:  S^T = K q^T,  O^T += V^T P^T.  Four row blocks of
 // 32 rows (two 16-column MFMA tiles) cover the tile's 128 rows.  For bfloat16
 // each row block has two wavefronts on the same SIMD that take alternate KV
-// stages (eight wavefronts per workgroup), so one wavefront's softmax runs
-// while the other's products occupy the matrix core; their partial results
-// are combined through LDS at the end with the usual log-sum-exp rescaling.
+// stages (eight wavefronts per workgroup), so that one can issue while the
+// other waits on a dependency; their partial results are combined through LDS
+// at the end with the usual log-sum-exp rescaling.
 //
 // Staging: pairs of KV pages (32 keys; K and V of two pages, 16 KiB for bf16
 // head_dim 128) go from HBM straight into a ring of kStages LDS buffers with
 // global->LDS loads, issued several rounds ahead of the stages being consumed,
 // one workgroup barrier per round.  Inside a buffer each 16-byte chunk of a
 // row sits at chunk ^ f(row), with f chosen per page kind (K or V) so that
-// the rows one read instruction touches fall in distinct banks.  V^T operands come from the transposing LDS read (ds_read_b64_tr_b16),
-// which hands each lane 4 consecutive keys of one column.  The sequence that
-// owns a tile is found by a binary search over query_start_loc ("Replacing
-// attention, reusing the rest": each threadgroup finds its request by binary
-// search over cu_seqlens).
+// the rows one read instruction touches fall in distinct banks.  V^T operands
+// come from the transposing LDS read (ds_read_b64_tr_b16), which hands each
+// lane 4 consecutive keys of one column.  A wavefront issues at most one
+// instruction per 4-cycle turn of its SIMD, so the transfer bookkeeping is
+// kept to a few scalar instructions per stage (pre-scaled page offsets in LDS,
+// scalar-base loads).  The sequence that owns a tile is found by a binary
+// search over query_start_loc ("Replacing attention, reusing the rest": each
+// threadgroup finds its request by binary search over cu_seqlens).
 #pragma once
 
 #include <type_traits>
@@ -196,9 +199,10 @@ __device__ __forceinline__ void unroll_rounds(F&& f) {
     }
 }
 
-// Block-table entries a workgroup stages in LDS (contexts up to 64K keys);
-// longer contexts use the LONG variant, which reads them through the scalar
-// data cache instead.
+// Block-table entries a workgroup stages in LDS, as pool offsets (contexts
+// up to 64K keys, pools whose offsets / 256 fit 32 bits); longer contexts and
+// larger pools use the LONG variant, which reads the block ids through the
+// scalar data cache instead.
 constexpr int kPrefillIdTable = 4096;
 
 template <typename T, int D, bool LONG>
@@ -589,7 +593,8 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     // of a row block.  Before the barrier this thread's loads of those stages
     // are complete; after it every wavefront is done with round rr - 1, whose
     // slots take the stages NS - SPLIT ahead.
-    // ids[j]: block ids of the stage the next round loads as its j-th
+    // ids[j]: what the transfers of the next round's j-th stage need (page
+    // offsets / 256, or block ids in the LONG variant)
     int2 ids[SPLIT];
     // Interior rounds (EDGE false) also lie far enough from the end that
     // every stage they wait for and issue exists: their wait is a constant and
