@@ -387,9 +387,67 @@ def bench_single(k, args):
         rec["extra"] = extra_prefill(min(args.steps, 20), args.warmup)
         rec["extra"]["verify_windows"] = extra_windows(min(args.steps, 20), args.warmup)
         rec["extra"]["pool_manager"] = extra_pool()
+    if not args.no_extra and k == 3:
+        rec["extra"] = {"split_parts": split_parts(min(args.steps, 20), args.warmup)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(st)
     return rec
+
+
+def split_parts(steps: int, warmup: int):
+    """The mixed step's decode part and its prefill chunks as two calls: back
+    to back on one stream, and at once on two streams (whether running the
+    HBM-bound and the MFMA-bound parts concurrently would pay)."""
+    mixed = W.config_step(3, poison=False)
+    ip = [i for i, n in enumerate(mixed.q_lens) if n > 1]
+    idc = [i for i, n in enumerate(mixed.q_lens) if n == 1]
+    pre = W.build_step("mixed-prefill-chunks", [mixed.seq_lens[i] for i in ip],
+                       [mixed.q_lens[i] for i in ip], 32, 8, 128, torch.bfloat16, 3000, poison=False)
+    dec = W.build_step("mixed-decode-part", [mixed.seq_lens[i] for i in idc], [1] * len(idc),
+                       32, 8, 128, torch.bfloat16, 3001, poison=False)
+    sp, sd = Step(pre, gen_device="cuda"), Step(dec, gen_device="cuda")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn):
+        ts = []
+        for r in range(steps + warmup):
+            flush.sum()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if r >= warmup:
+                ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def serial():
+        sd.attention()
+        sp.attention()
+
+    def concurrent():
+        cur = torch.cuda.current_stream()
+        e = torch.cuda.Event()
+        e.record(cur)
+        s1.wait_event(e)
+        s2.wait_event(e)
+        with torch.cuda.stream(s1):
+            sd.attention()
+        with torch.cuda.stream(s2):
+            sp.attention()
+        cur.wait_stream(s1)
+        cur.wait_stream(s2)
+
+    res = {"decode_part_ms": timed(sd.attention), "prefill_part_ms": timed(sp.attention),
+           "back_to_back_ms": timed(serial), "two_streams_ms": timed(concurrent)}
+    log(f"split mixed step: decode part {res['decode_part_ms']:.4f} ms, prefill part "
+        f"{res['prefill_part_ms']:.4f} ms, back to back {res['back_to_back_ms']:.4f} ms, "
+        f"two streams {res['two_streams_ms']:.4f} ms")
+    del sp, sd, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def agent_loop(run):
