@@ -127,6 +127,10 @@ size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqle
  * apply the same causal rule.  A sequence with zero query tokens contributes
  * nothing.
  *
+ * scale must be finite and positive (a softmax temperature; the kernels bound
+ * the running maximum of the scaled logits through the maximum of the raw
+ * ones), else PKV_E_ARG.
+ *
  * Supported: dtype F32/BF16 (q, pools and out share it), head_dim 64 or 128,
  * block_size 16, num_q_heads % num_kv_heads == 0 and 1 <= group size <= 16,
  * and num_seqs <= 16384; otherwise PKV_E_UNSUPPORTED.

@@ -248,7 +248,8 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
         return fail(PKV_E_ARG, "max_seqlen_k %d exceeds the block-table width (%d pages of %d)",
                     max_seqlen_k, max_blocks_per_seq, block_size);
     if (total_q > 0x7fffffffLL) return fail(PKV_E_ARG, "total_q too large");
-    if (!std::isfinite(scale)) return fail(PKV_E_ARG, "scale is not finite");
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(PKV_E_ARG, "scale %g is not finite and positive", (double)scale);
     const size_t eb = elem_bytes(dtype);
     const size_t io_bytes = (size_t)total_q * num_q_heads * head_dim * eb;
     const size_t pool_bytes = (size_t)num_blocks * num_kv_heads * block_size * head_dim * eb;

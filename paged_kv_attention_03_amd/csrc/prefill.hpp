@@ -386,6 +386,11 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         for (int t = 0; t < Gm::NT; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float m_run[2] = {-INFINITY, -INFINITY};
+    // derived from m_run, updated only when it is raised: the threshold past
+    // which a logit raises it, and the exponent offset -m_run (0 while no key
+    // has been seen)
+    float m_thr[2] = {-INFINITY, -INFINITY};
+    float m_off[2] = {0.f, 0.f};
 
     // Per-lane LDS offsets inside the ring, fixed for the whole loop; they
     // include this wavefront's slot within a round (stage st sits in slot
@@ -511,7 +516,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                     sv[nt][x * 4 + t] = v;
                     mt = fmaxf(mt, v);
                 }
-            grow |= mt * p.scale_log2 > m_run[nt] + 8.f;
+            grow |= mt * p.scale_log2 > m_thr[nt];
         }
         if (__any(grow)) {
             // exact column maxima, then rescale what was accumulated so far
@@ -525,6 +530,8 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
                 const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
                 const float alpha = fast_exp2(m_run[nt] - m_use);
                 m_run[nt] = m_new;
+                m_thr[nt] = m_new + 8.f;
+                m_off[nt] = -m_use;
                 lsum[nt] *= alpha;
 #pragma unroll
                 for (int t = 0; t < Gm::NT; ++t) acc[nt][t] *= alpha;
@@ -534,10 +541,9 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         float pv[2][8];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                pv[nt][t] = fast_exp2(__builtin_fmaf(sv[nt][t], p.scale_log2, -m_use));
+                pv[nt][t] = fast_exp2(__builtin_fmaf(sv[nt][t], p.scale_log2, m_off[nt]));
             if constexpr (kBF)
                 pb[nt] = u32x4{pack_bf16(pv[nt][0], pv[nt][1]), pack_bf16(pv[nt][2], pv[nt][3]),
                                pack_bf16(pv[nt][4], pv[nt][5]), pack_bf16(pv[nt][6], pv[nt][7])};

@@ -62,6 +62,8 @@ def _attn(lib, **over):
     (dict(nb=0), pkv.PKV_E_ARG),
     (dict(num_seqs=-1), pkv.PKV_E_ARG),
     (dict(scale=float("nan")), pkv.PKV_E_ARG),
+    (dict(scale=0.0), pkv.PKV_E_ARG),
+    (dict(scale=-0.125), pkv.PKV_E_ARG),
     (dict(num_seqs=16385, total_q=16385, max_blocks=8), pkv.PKV_E_UNSUPPORTED),
 ])
 def test_attention_rejects_invalid_arguments(lib, over, code):
