@@ -3,6 +3,8 @@ dtype, batch size, context lengths (page edges favoured), query counts (decodes,
 verify windows, chunks), left padding, shared prefixes, extra block-table width
 and pool slack all drawn from one seed per case.  Pools are NaN outside the
 valid rows.  Each case prints its recipe before it runs."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,8 @@ from paged_kv_attention_03_amd import workloads as W
 from tests.gpu_helpers import check_close, gpu_attention, gpu_pools, log, raw_bits
 from tests.helpers import oracle_pools, oracle_step
 
-CASES = 24
+# PKV_RANDOM_CASES widens the sweep for a one-off run (the suite runs 24)
+CASES = int(os.environ.get("PKV_RANDOM_CASES", "24"))
 
 
 def _recipe(seed):
