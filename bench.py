@@ -179,15 +179,17 @@ def measured_traffic(name: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(st, budget_s: float = 15.0):
+def cpu_baseline(st, budget_s: float = 10.0):
     """The float64 oracle on the host cores over the first sequences of the
-    workload, batched 16 sequences per call, until about ``budget_s`` seconds
-    of oracle time.  Only the oracle calls are timed (page gather + math)."""
+    workload (up to ``budget_s`` seconds for one pass), batched 16 sequences
+    per call; the pass is repeated until about ``budget_s`` seconds of oracle
+    time (3 to 10 passes) and the median pass is reported.  Only the oracle
+    calls are timed (page gather + math)."""
     import oracle
     q_dev = st.make_q("cuda")
-    spent, covered, seqs = 0.0, 0, 0
     qsl = st.query_start_loc()
-    while seqs < st.num_seqs and spent < budget_s:
+    batches, covered, seqs, first = [], 0, 0, 0.0
+    while seqs < st.num_seqs and first < budget_s:
         batch = list(range(seqs, min(seqs + 16, st.num_seqs)))
         ks, vs, bts, lens, qs, qls = [], [], [], [], [], []
         page0 = 0
@@ -210,20 +212,30 @@ def cpu_baseline(st, budget_s: float = 15.0):
         bt = np.zeros((len(batch), width), np.int32)
         for i, b in enumerate(bts):
             bt[i, :len(b)] = b
-        qcat = torch.cat(qs)
-        qsl_b = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+        args = (torch.cat(qs), kpool, vpool, bt, lens,
+                np.concatenate([[0], np.cumsum(qls)]).astype(np.int32), st.scale)
         t0 = time.perf_counter()
-        oracle.oracle_attention(qcat, kpool, vpool, bt, lens, qsl_b, st.scale)
-        spent += time.perf_counter() - t0
+        oracle.oracle_attention(*args)
+        first += time.perf_counter() - t0
+        batches.append(args)
         covered += sum(lens)
         seqs += len(batch)
-        del kpool, vpool
+    passes, spent = [first], first
+    while len(passes) < 10 and (len(passes) < 3 or spent < budget_s):
+        t0 = time.perf_counter()
+        for args in batches:
+            oracle.oracle_attention(*args)
+        passes.append(time.perf_counter() - t0)
+        spent += passes[-1]
+    del batches
+    med = float(np.median(passes))
     e = 2 if st.dtype == torch.bfloat16 else 4
     kvb = covered * 2 * st.num_kv_heads * st.head_dim * e
-    return {"value": kvb / spent / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "tokens_per_s": seqs / spent,
+    return {"value": kvb / med / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "tokens_per_s": seqs / med,
             "sample": f"first {seqs} of {st.num_seqs} sequences ({covered} keys, "
-                      f"{kvb / 1e9:.2f} GB of K/V), {spent:.1f} s of oracle time"}
+                      f"{kvb / 1e9:.2f} GB of K/V); median of {len(passes)} passes, "
+                      f"{spent:.1f} s of oracle time"}
 
 
 def extra_prefill(steps: int, warmup: int):
