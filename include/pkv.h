@@ -147,6 +147,55 @@ int pkv_attention(void *out, const void *q, const void *k_pool, const void *v_po
                   size_t workspace_bytes, void *stream);
 
 /*
+ * pkv_attention_shared_prefix -- pkv_attention for a step in which groups of
+ * decode sequences share their first keys through common pages, reading
+ * each group's shared pages once per kv head instead of once per sequence.
+ *
+ * Requests that share a prompt prefix keep it in shared pages (vllm-metal
+ * v0.4.0 release post, "Prefix caching on hybrid models"; the vllm-mlx paper
+ * summary, results: prefix caching on 512-token shared prefixes).  Attention
+ * over a sequence's keys is the log-sum-exp combination of attention over the
+ * shared prefix and over the rest, so the result is the same as
+ * pkv_attention's (up to rounding order): the prefix of each group is
+ * attended once for all its members' query rows (matrix-core tiles, chunks
+ * of the prefix in parallel), each member's own keys by the decode pass,
+ * which starts from the prefix's softmax states.
+ *
+ * prefix_group [num_seqs] int32 (device): the group of sequence s in
+ * [0, num_groups), or -1.  prefix_len [num_groups] int32 (device): the
+ * group's shared keys, a multiple of block_size, at most max_prefix_len.
+ * Contract for a member s of group g: one query token (a decode), seq_lens[s]
+ * > prefix_len[g], and its first prefix_len[g] / block_size block-table
+ * entries are the group's shared pages (the same physical ids in every
+ * member's row).  Members past the first max_group_size of a group (in
+ * sequence order), and sequences that break the token or length condition,
+ * are computed as plain sequences.  Other sequences of the step (prefill
+ * chunks, verify windows, unshared decodes) are computed as by pkv_attention.
+ * kv_start is not taken (no left padding in such a step).
+ *
+ * Host bounds: max_group_size > 0, max_prefix_len a positive multiple of
+ * block_size below max_seqlen_k, 0 <= num_groups <= 1024 (num_groups == 0:
+ * exactly pkv_attention).  Workspace: at least
+ * pkv_attention_shared_prefix_workspace_size(...) bytes with the same bounds.
+ * Errors and every other argument as for pkv_attention.
+ */
+size_t pkv_attention_shared_prefix_workspace_size(int num_seqs, int64_t total_q, int max_seqlen_q,
+                                                  int max_seqlen_k, int num_q_heads,
+                                                  int num_kv_heads, int head_dim, int block_size,
+                                                  pkv_dtype_t dtype, int num_groups,
+                                                  int max_group_size, int max_prefix_len);
+
+int pkv_attention_shared_prefix(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                const int32_t *block_tables, const int32_t *seq_lens,
+                                const int32_t *query_start_loc, const int32_t *prefix_group,
+                                const int32_t *prefix_len, int num_groups, int max_group_size,
+                                int max_prefix_len, int num_seqs, int64_t total_q,
+                                int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int64_t num_blocks, float scale, pkv_dtype_t dtype,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pkv_check_metadata -- validate HOST copies of the step metadata against the
  * contract above: query_start_loc starts at 0, is non-decreasing and ends at
  * total_q; 0 <= kv_start[s] <= seq_lens[s]; each sequence's query count is at
@@ -158,6 +207,19 @@ int pkv_check_metadata(const int32_t *block_tables, const int32_t *seq_lens,
                        const int32_t *query_start_loc, const int32_t *kv_start, int num_seqs,
                        int64_t total_q, int max_blocks_per_seq, int block_size,
                        int64_t num_blocks);
+
+/*
+ * pkv_check_shared_prefix -- validate HOST copies of a shared-prefix step's
+ * groups against the contract of pkv_attention_shared_prefix: group ids in
+ * [-1, num_groups); prefix lengths multiples of block_size, at most
+ * max_prefix_len and inside the block table; every member a decode (one query
+ * token) with more keys than its prefix; all members of a group list the same
+ * physical pages for the prefix.  Returns PKV_OK or PKV_E_METADATA.
+ */
+int pkv_check_shared_prefix(const int32_t *block_tables, const int32_t *seq_lens,
+                            const int32_t *query_start_loc, const int32_t *prefix_group,
+                            const int32_t *prefix_len, int num_seqs, int num_groups,
+                            int max_blocks_per_seq, int block_size, int max_prefix_len);
 
 /*
  * pkv_check_slots -- validate a HOST copy of a slot mapping: every

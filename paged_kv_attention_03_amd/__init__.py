@@ -9,6 +9,9 @@ raises at the first call.
     pkv_append(k_new, v_new, k_pool, v_pool, slot_mapping)
     out = pkv_attention(q, k_pool, v_pool, block_tables, seq_lens,
                         query_start_loc, scale, max_seqlen_q=..., max_seqlen_k=...)
+    out = pkv_attention_shared_prefix(q, k_pool, v_pool, block_tables, seq_lens,
+                                      query_start_loc, scale, prefix_group, prefix_len,
+                                      max_group_size=..., max_prefix_len=..., ...)
 """
 from __future__ import annotations
 
@@ -20,7 +23,9 @@ import torch
 
 __all__ = [
     "PKV_F32", "PKV_BF16", "PkvError", "pkv_append", "pkv_attention",
-    "pkv_attention_workspace_size", "pkv_check_metadata", "pkv_check_slots", "pkv_last_error",
+    "pkv_attention_workspace_size", "pkv_attention_shared_prefix",
+    "pkv_attention_shared_prefix_workspace_size", "pkv_check_shared_prefix",
+    "pkv_check_metadata", "pkv_check_slots", "pkv_last_error",
     "pkv_copy_blocks", "PagePool", "library_path", "load_library",
 ]
 
@@ -69,6 +74,15 @@ def load_library():
     lib.pkv_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                   i32, i32, i32, i64, ctypes.c_float, i32, vp, sz, vp]
     lib.pkv_attention.restype = i32
+    lib.pkv_attention_shared_prefix_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32,
+                                                               i32, i32, i32, i32, i32]
+    lib.pkv_attention_shared_prefix_workspace_size.restype = sz
+    lib.pkv_attention_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                i32, i64, i32, i32, i32, i32, i32, i32, i32,
+                                                i64, ctypes.c_float, i32, vp, sz, vp]
+    lib.pkv_attention_shared_prefix.restype = i32
+    lib.pkv_check_shared_prefix.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32]
+    lib.pkv_check_shared_prefix.restype = i32
     lib.pkv_check_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i64]
     lib.pkv_check_metadata.restype = i32
     lib.pkv_check_slots.argtypes = [vp, i64, i32, i64]
@@ -218,6 +232,90 @@ def pkv_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                              hq, hkv, d, bs, nb, float(scale), dt, ws_ptr, ws_bytes,
                              _stream(q.device, stream)))
     return out
+
+
+def pkv_attention_shared_prefix_workspace_size(num_seqs: int, total_q: int, max_seqlen_q: int,
+                                               max_seqlen_k: int, num_q_heads: int,
+                                               num_kv_heads: int, head_dim: int,
+                                               block_size: int = 16,
+                                               dtype: torch.dtype = torch.bfloat16, *,
+                                               num_groups: int, max_group_size: int,
+                                               max_prefix_len: int) -> int:
+    return int(load_library().pkv_attention_shared_prefix_workspace_size(
+        num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim,
+        block_size, _dtype_code(dtype), num_groups, max_group_size, max_prefix_len))
+
+
+def pkv_attention_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                query_start_loc: torch.Tensor, scale: float,
+                                prefix_group: torch.Tensor, prefix_len: torch.Tensor, *,
+                                max_group_size: int, max_prefix_len: int, max_seqlen_q: int,
+                                max_seqlen_k: int, out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None,
+                                stream=None) -> torch.Tensor:
+    """pkv_attention for a step whose decode sequences share prefixes in groups:
+    prefix_group [S] int32 (group or -1), prefix_len [num_groups] int32 (shared
+    keys, multiples of the page size).  Same result as pkv_attention; each
+    group's shared pages are read once per kv head."""
+    lib = load_library()
+    dt = _dtype_code(q.dtype)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [total_q, Hq, D] and pools [num_blocks, Hkv, bs, D]")
+    total_q, hq, d = q.shape
+    nb, hkv, bs, d2 = k_pool.shape
+    if d2 != d:
+        raise ValueError("head_dim of q and pools differ")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    ns, max_blocks = block_tables.shape
+    if seq_lens.shape != (ns,) or query_start_loc.shape != (ns + 1,):
+        raise ValueError("seq_lens must be [num_seqs] and query_start_loc [num_seqs + 1]")
+    if prefix_group.shape != (ns,) or prefix_len.dim() != 1:
+        raise ValueError("prefix_group must be [num_seqs] and prefix_len [num_groups]")
+    ng = prefix_len.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = pkv_attention_shared_prefix_workspace_size(
+        ns, total_q, max_seqlen_q, max_seqlen_k, hq, hkv, d, bs, q.dtype, num_groups=ng,
+        max_group_size=max_group_size, max_prefix_len=max_prefix_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ptrs = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype),
+            _dev(v_pool, "v_pool", q.dtype), _dev(block_tables, "block_tables", torch.int32),
+            _dev(seq_lens, "seq_lens", torch.int32),
+            _dev(query_start_loc, "query_start_loc", torch.int32),
+            _dev(prefix_group, "prefix_group", torch.int32),
+            _dev(prefix_len, "prefix_len", torch.int32))
+    if os.environ.get("PKV_CHECK") == "1":
+        pkv_check_metadata(block_tables, seq_lens, query_start_loc, None, total_q, bs, nb)
+        pkv_check_shared_prefix(block_tables, seq_lens, query_start_loc, prefix_group,
+                                prefix_len, bs, max_prefix_len)
+    _raise(lib.pkv_attention_shared_prefix(
+        *ptrs, ng, int(max_group_size), int(max_prefix_len), ns, total_q, max_blocks,
+        int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), dt, ws_ptr,
+        ws_bytes, _stream(q.device, stream)))
+    return out
+
+
+def pkv_check_shared_prefix(block_tables, seq_lens, query_start_loc, prefix_group, prefix_len,
+                            block_size: int, max_prefix_len: int) -> None:
+    """Validate host copies of a shared-prefix step's groups; raises PkvError."""
+    bt = _host_i32(block_tables)
+    sl = _host_i32(seq_lens)
+    qsl = _host_i32(query_start_loc)
+    pg = _host_i32(prefix_group)
+    pl = _host_i32(prefix_len)
+    ns = sl.shape[0]
+    if bt.ndim != 2 or bt.shape[0] != ns or qsl.shape != (ns + 1,) or pg.shape != (ns,):
+        raise ValueError("metadata shapes disagree")
+    _raise(load_library().pkv_check_shared_prefix(
+        bt.ctypes.data, sl.ctypes.data, qsl.ctypes.data, pg.ctypes.data, pl.ctypes.data, ns,
+        pl.shape[0], bt.shape[1], block_size, max_prefix_len))
 
 
 def _host_i32(x):

@@ -115,6 +115,14 @@ struct DecodeParams {
     int ncol;       // G * wmax columns per partial slot
     int64_t num_blocks;
     float scale_log2;  // softmax scale * log2(e)
+    // Steps whose sequences share prefixes (null otherwise): per sequence, the
+    // softmax state of its shared prefix in `state` -- x: its state row (per
+    // query head; x < 0: none).  The first piece of each of the sequence's
+    // segments starts from it (the decode pass itself reads only the keys
+    // after the prefix).
+    const int4* prefix_states;
+    const float* state;  // [state_rows][Hq][kStateStride]
+    int64_t state_rows;
 };
 
 struct MergeParams {
@@ -264,7 +272,9 @@ struct PairRegs {
     u32x4 v[2][DecodeGeom<T, D>::VCH];
 };
 
-template <typename T, int D>
+// PS: the step has shared-prefix states to start from (a separate
+// instantiation, so that plain steps run the kernel without that code).
+template <typename T, int D, bool PS>
 __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel(DecodeParams p) {
     using Gm = DecodeGeom<T, D>;
     constexpr bool kBF = !__is_same(T, float);
@@ -511,6 +521,21 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
             for (int t = 0; t < Gm::NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             m_run = -INFINITY;
             l_run = 0.f;
+            if (PS && ppi == 0) {
+                // the segment's first piece starts from the prefix's state
+                // (its chunks already folded into the first chunk's row)
+                const int4 cd = p.prefix_states[ps];
+                if (cd.x >= 0 && hvalid) {
+                    const int h = pg_ * p.G + col - ctok * p.G;
+                    const int64_t r = (cd.x < p.state_rows) ? cd.x : 0;
+                    const float* sr = p.state + (r * p.Hq + h) * kStateStride<D>;
+#pragma unroll
+                    for (int t = 0; t < Gm::NT; ++t)
+                        acc[t] = *reinterpret_cast<const f32x4*>(sr + t * 16 + grp * 4);
+                    m_run = sr[D];
+                    l_run = grp == 0 ? sr[D + 1] : 0.f;  // summed over the column's lanes at the end
+                }
+            }
         };
 
         auto finish_piece = [&]() {

@@ -20,6 +20,7 @@
 #include "append.hpp"
 #include "decode.hpp"
 #include "prefill.hpp"
+#include "cascade.hpp"
 #include "pool.hpp"
 
 struct pkv_pool {
@@ -107,6 +108,51 @@ Plan make_plan(int num_seqs, int num_kv_heads, int head_dim, int group, int max_
     return pl;
 }
 
+// Shared-prefix steps: the workspace after the plain plan holds the setup
+// kernel's outputs and the prefix states (every region 256-byte aligned):
+//   kv_eff int32[num_seqs], prefix_states int4[num_seqs],
+//   v_qsl int32[V + 1], v_lens, v_start, v_row int32[V], v_qrows int32[V * M],
+//   state float[V * M][Hq][D + 4],
+// V = groups x chunks per group, M = max_group_size.  Chunks are sized so
+// that the prefix pass has about one workgroup per CU: groups x chunks x kv
+// heads ~ 256, at least 64 keys, a multiple of 32 (whole page pairs).
+struct CascadePlan {
+    int chunk = 0, max_chunks = 0, V = 0;
+    int64_t vtokens = 0;
+    size_t off_kv = 0, off_states = 0, off_vqsl = 0, off_vlens = 0, off_vstart = 0, off_vrow = 0,
+           off_vqrows = 0, off_state = 0, total = 0;
+};
+
+CascadePlan make_cascade_plan(size_t base, int num_seqs, int num_groups, int max_group_size,
+                              int max_prefix_len, int num_q_heads, int num_kv_heads, int head_dim) {
+    CascadePlan c;
+    const int64_t want = ((int64_t)max_prefix_len * num_groups * num_kv_heads + 255) / 256;
+    c.chunk = (int)std::max<int64_t>(64, (want + 31) / 32 * 32);
+    c.max_chunks = (max_prefix_len + c.chunk - 1) / c.chunk;
+    c.V = num_groups * c.max_chunks;
+    c.vtokens = (int64_t)c.V * max_group_size;
+    size_t off = align256(base);
+    c.off_kv = off;
+    off = align256(off + sizeof(int32_t) * (size_t)num_seqs);
+    c.off_states = off;
+    off = align256(off + sizeof(int4) * (size_t)num_seqs);
+    c.off_vqsl = off;
+    off = align256(off + sizeof(int32_t) * (size_t)(c.V + 1));
+    c.off_vlens = off;
+    off = align256(off + sizeof(int32_t) * (size_t)c.V);
+    c.off_vstart = off;
+    off = align256(off + sizeof(int32_t) * (size_t)c.V);
+    c.off_vrow = off;
+    off = align256(off + sizeof(int32_t) * (size_t)c.V);
+    c.off_vqrows = off;
+    off = align256(off + sizeof(int32_t) * (size_t)c.vtokens);
+    c.off_state = off;
+    off = align256(off + sizeof(float) * (size_t)c.vtokens * num_q_heads *
+                             (size_t)(head_dim + 4));
+    c.total = off;
+    return c;
+}
+
 int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                  pkv_dtype_t dtype) {
     if (dtype != PKV_F32 && dtype != PKV_BF16)
@@ -126,6 +172,27 @@ int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size
     return PKV_OK;
 }
 
+// One tile per (sequence, kv head, 128/G query tokens); the grid is sized from
+// host bounds and tiles past a sequence's tokens return at once.
+template <typename T, int D>
+int launch_prefill(const pkv::PrefillParams& pp, hipStream_t stream, const char* what) {
+    const long tiles = pp.state ? (long)pp.num_seqs * pp.sp_tiles
+                                : (pp.total_q + pp.tile_tokens - 1) / pp.tile_tokens + pp.num_seqs;
+    // a tile's pages: at most ceil(max_seqlen_k / 16) + 1, rounded up to pairs
+    // (or a pool whose (page, kv head) offsets / 256 exceed 32 bits)
+    const bool long_ctx =
+        ((long)pp.max_seqlen_k + kBlock - 1) / kBlock + 2 > pkv::kPrefillIdTable ||
+        (uint64_t)pp.num_blocks * (uint64_t)pp.Hkv * (pkv::PrefillGeom<T, D>::PAGE / 256) >
+            0xffffffffull;
+    if (long_ctx)
+        hipLaunchKernelGGL((pkv::prefill_kernel<T, D, true>), dim3((unsigned)(tiles * pp.Hkv)),
+                           dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
+    else
+        hipLaunchKernelGGL((pkv::prefill_kernel<T, D, false>), dim3((unsigned)(tiles * pp.Hkv)),
+                           dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
+    return hip_status(what);
+}
+
 template <typename T, int D>
 int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
                      const pkv::MergeParams& mp, const pkv::PrefillParams& pp, int max_seqlen_q,
@@ -136,28 +203,261 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
         hipLaunchKernelGGL(pkv::decode_plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, stream, pl);
         if (int rc = hip_status("decode plan launch")) return rc;
     }
-    hipLaunchKernelGGL((pkv::decode_kernel<T, D>), dim3(pkv::kDecodeWaves), dim3(64), 0, stream, dp);
+    if (dp.prefix_states)
+        hipLaunchKernelGGL((pkv::decode_kernel<T, D, true>), dim3(pkv::kDecodeWaves), dim3(64), 0,
+                           stream, dp);
+    else
+        hipLaunchKernelGGL((pkv::decode_kernel<T, D, false>), dim3(pkv::kDecodeWaves), dim3(64), 0,
+                           stream, dp);
     if (int rc = hip_status("decode launch")) return rc;
     hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)), dim3(64),
                        0, stream, mp);
     if (int rc = hip_status("merge launch")) return rc;
-    if (max_seqlen_q > pl.wmax) {  // longer sequences: chunked prefill
-        const long tiles = (total_q + pp.tile_tokens - 1) / pp.tile_tokens + num_seqs;
-        // a tile's pages: at most ceil(max_seqlen_k / 16) + 1, rounded up to pairs
-        // (or a pool whose (page, kv head) offsets / 256 exceed 32 bits)
-        const bool long_ctx =
-            ((long)pp.max_seqlen_k + kBlock - 1) / kBlock + 2 > pkv::kPrefillIdTable ||
-            (uint64_t)pp.num_blocks * (uint64_t)pp.Hkv * (pkv::PrefillGeom<T, D>::PAGE / 256) >
-                0xffffffffull;
-        if (long_ctx)
-            hipLaunchKernelGGL((pkv::prefill_kernel<T, D, true>), dim3((unsigned)(tiles * pp.Hkv)),
-                               dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
-        else
-            hipLaunchKernelGGL((pkv::prefill_kernel<T, D, false>), dim3((unsigned)(tiles * pp.Hkv)),
-                               dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
-        if (int rc = hip_status("prefill launch")) return rc;
+    if (max_seqlen_q > pl.wmax)  // longer sequences: chunked prefill
+        return launch_prefill<T, D>(pp, stream, "prefill launch");
+    return PKV_OK;
+}
+
+// Shared-prefix steps, ahead of the plain launches: the setup kernel, then
+// the prefix states of every (group, chunk, kv head) from the prefill kernel.
+template <typename T, int D>
+int launch_prefix_pass(const pkv::CascadeParams& cp, const pkv::PrefillParams& spp,
+                       const pkv::StateCombineParams& sc, bool combine, hipStream_t stream) {
+    hipLaunchKernelGGL(pkv::cascade_setup_kernel, dim3(1), dim3(pkv::kCascadeThreads),
+                       pkv::cascade_setup_lds(cp.num_seqs, cp.num_groups), stream, cp);
+    if (int rc = hip_status("shared-prefix setup launch")) return rc;
+    if (int rc = launch_prefill<T, D>(spp, stream, "shared-prefix state launch")) return rc;
+    if (combine) {  // prefixes of more than one chunk
+        hipLaunchKernelGGL((pkv::state_combine_kernel<D>), dim3((unsigned)((long)sc.Hq * sc.num_seqs)),
+                           dim3(64), 0, stream, sc);
+        if (int rc = hip_status("shared-prefix combine launch")) return rc;
     }
     return PKV_OK;
+}
+
+// Shared-prefix groups of a step (pkv_attention_shared_prefix).
+struct PrefixArgs {
+    const int32_t* prefix_group;
+    const int32_t* prefix_len;
+    int num_groups;
+    int max_group_size;
+    int max_prefix_len;
+};
+
+int attention_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_tables, const int32_t* seq_lens,
+                   const int32_t* query_start_loc, const int32_t* kv_start, int num_seqs,
+                   int64_t total_q, int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
+                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                   int64_t num_blocks, float scale, pkv_dtype_t dtype, void* workspace,
+                   size_t workspace_bytes, void* stream, const PrefixArgs* pa) {
+    if (int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype)) return rc;
+    if (num_seqs < 0) return fail(PKV_E_ARG, "num_seqs %d < 0", num_seqs);
+    if (total_q < 0) return fail(PKV_E_ARG, "total_q %lld < 0", (long long)total_q);
+    if (num_seqs == 0 || total_q == 0) return ok();
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc)
+        return fail(PKV_E_ARG, "null pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKV_E_ARG, "q, out and the pools must be 16-byte aligned");
+    if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "max_blocks_per_seq %d <= 0", max_blocks_per_seq);
+    if (num_blocks <= 0) return fail(PKV_E_ARG, "num_blocks %lld <= 0", (long long)num_blocks);
+    if (max_seqlen_q <= 0 || max_seqlen_k <= 0)
+        return fail(PKV_E_ARG, "max_seqlen_q %d and max_seqlen_k %d must be positive", max_seqlen_q,
+                    max_seqlen_k);
+    if (max_seqlen_q > max_seqlen_k)
+        return fail(PKV_E_ARG, "max_seqlen_q %d > max_seqlen_k %d", max_seqlen_q, max_seqlen_k);
+    if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PKV_E_ARG, "max_seqlen_k %d exceeds the block-table width (%d pages of %d)",
+                    max_seqlen_k, max_blocks_per_seq, block_size);
+    if (total_q > 0x7fffffffLL) return fail(PKV_E_ARG, "total_q too large");
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(PKV_E_ARG, "scale %g is not finite and positive", (double)scale);
+    const size_t eb = elem_bytes(dtype);
+    const size_t io_bytes = (size_t)total_q * num_q_heads * head_dim * eb;
+    const size_t pool_bytes = (size_t)num_blocks * num_kv_heads * block_size * head_dim * eb;
+    if (overlaps(out, io_bytes, q, io_bytes) || overlaps(out, io_bytes, k_pool, pool_bytes) ||
+        overlaps(out, io_bytes, v_pool, pool_bytes))
+        return fail(PKV_E_ARG, "out must not alias q or the pools");
+
+    if (num_seqs > pkv::kMaxDecodeSeqs)
+        return fail(PKV_E_UNSUPPORTED, "num_seqs %d > %d is not supported", num_seqs,
+                    pkv::kMaxDecodeSeqs);
+    const int G = num_q_heads / num_kv_heads;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, G, max_seqlen_q);
+    const bool cascade = pa != nullptr && pa->num_groups > 0;
+    CascadePlan cpl;
+    if (cascade)
+        cpl = make_cascade_plan(pl.total, num_seqs, pa->num_groups, pa->max_group_size,
+                                pa->max_prefix_len, num_q_heads, num_kv_heads, head_dim);
+    const size_t need = cascade ? cpl.total : pl.total;
+    if (!workspace || workspace_bytes < need)
+        return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned16(workspace)) return fail(PKV_E_ARG, "workspace must be 16-byte aligned");
+    if (overlaps(workspace, need, out, io_bytes))
+        return fail(PKV_E_ARG, "workspace must not alias out");
+    const float scale_log2 = scale * 1.4426950408889634f;
+    char* wsb = static_cast<char*>(workspace);
+    int32_t* prefix = reinterpret_cast<int32_t*>(wsb + pl.off_prefix);
+    int32_t* pbegin = reinterpret_cast<int32_t*>(wsb + pl.off_pbegin);
+    pkv::Portion* portions = reinterpret_cast<pkv::Portion*>(wsb + pl.off_portions);
+    float* ws_o = reinterpret_cast<float*>(wsb + pl.off_o);
+    float* ws_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
+
+    pkv::PlanParams plp{};
+    plp.seq_lens = seq_lens;
+    plp.qsl = query_start_loc;
+    plp.kv_start = kv_start;
+    plp.num_seqs = num_seqs;
+    plp.Hkv = num_kv_heads;
+    plp.max_seqlen_k = max_seqlen_k;
+    plp.max_blocks = max_blocks_per_seq;
+    plp.wmax = pl.wmax;
+    plp.total_q = total_q;
+    plp.pair_prefix = prefix;
+    plp.portion_begin = pbegin;
+    plp.portions = portions;
+
+    pkv::DecodeParams dp{};
+    dp.out = out;
+    dp.q = q;
+    dp.k_pool = k_pool;
+    dp.v_pool = v_pool;
+    dp.block_tables = block_tables;
+    dp.portion_begin = pbegin;
+    dp.portions = portions;
+    dp.ws_o = ws_o;
+    dp.ws_ml = ws_ml;
+    dp.max_blocks = max_blocks_per_seq;
+    dp.Hq = num_q_heads;
+    dp.Hkv = num_kv_heads;
+    dp.G = G;
+    dp.gmagic = (65536 + G - 1) / G;
+    dp.ncol = G * pl.wmax;
+    dp.num_blocks = num_blocks;
+    dp.inline_plan = num_seqs <= pkv::kInlinePlanSeqs ? 1 : 0;
+    dp.seq_lens = seq_lens;
+    dp.qsl = query_start_loc;
+    dp.kv_start = kv_start;
+    dp.num_seqs = num_seqs;
+    dp.max_seqlen_k = max_seqlen_k;
+    dp.wmax = pl.wmax;
+    dp.total_q = total_q;
+    dp.pair_prefix = prefix;
+    dp.scale_log2 = scale_log2;
+
+    pkv::MergeParams mp{};
+    mp.out = out;
+    mp.ws_o = ws_o;
+    mp.ws_ml = ws_ml;
+    mp.pair_prefix = prefix;
+    mp.qsl = query_start_loc;
+    mp.num_seqs = num_seqs;
+    mp.Hq = num_q_heads;
+    mp.Hkv = num_kv_heads;
+    mp.G = G;
+    mp.ncol = G * pl.wmax;
+
+    pkv::PrefillParams pp{};
+    pp.out = out;
+    pp.q = q;
+    pp.k_pool = k_pool;
+    pp.v_pool = v_pool;
+    pp.block_tables = block_tables;
+    pp.seq_lens = seq_lens;
+    pp.qsl = query_start_loc;
+    pp.kv_start = kv_start;
+    pp.num_seqs = num_seqs;
+    pp.max_blocks = max_blocks_per_seq;
+    pp.Hq = num_q_heads;
+    pp.Hkv = num_kv_heads;
+    pp.G = G;
+    pp.tile_tokens = pl.prefill_tile_tokens;
+    pp.min_q = pl.wmax + 1;
+    pp.max_seqlen_k = max_seqlen_k;
+    pp.total_q = total_q;
+    pp.num_blocks = num_blocks;
+    pp.scale_log2 = scale_log2;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc;
+    if (cascade) {
+        // the prefix pass's inputs and states live after the plain plan; the
+        // plain launches then skip each member's prefix keys (kv_eff) and
+        // start its decode segments from the prefix states
+        int32_t* kv_eff = reinterpret_cast<int32_t*>(wsb + cpl.off_kv);
+        int4* states = reinterpret_cast<int4*>(wsb + cpl.off_states);
+        int32_t* v_qsl = reinterpret_cast<int32_t*>(wsb + cpl.off_vqsl);
+        int32_t* v_lens = reinterpret_cast<int32_t*>(wsb + cpl.off_vlens);
+        int32_t* v_start = reinterpret_cast<int32_t*>(wsb + cpl.off_vstart);
+        int32_t* v_row = reinterpret_cast<int32_t*>(wsb + cpl.off_vrow);
+        int32_t* v_qrows = reinterpret_cast<int32_t*>(wsb + cpl.off_vqrows);
+        float* state = reinterpret_cast<float*>(wsb + cpl.off_state);
+
+        pkv::CascadeParams cp{};
+        cp.prefix_group = pa->prefix_group;
+        cp.prefix_len = pa->prefix_len;
+        cp.qsl = query_start_loc;
+        cp.seq_lens = seq_lens;
+        cp.num_seqs = num_seqs;
+        cp.num_groups = pa->num_groups;
+        cp.max_members = pa->max_group_size;
+        cp.max_chunks = cpl.max_chunks;
+        cp.chunk = cpl.chunk;
+        cp.total_q = total_q;
+        cp.kv_eff = kv_eff;
+        cp.prefix_states = states;
+        cp.v_qsl = v_qsl;
+        cp.v_lens = v_lens;
+        cp.v_start = v_start;
+        cp.v_row = v_row;
+        cp.v_qrows = v_qrows;
+
+        pkv::PrefillParams spp = pp;
+        spp.out = nullptr;
+        spp.seq_lens = v_lens;
+        spp.qsl = v_qsl;
+        spp.kv_start = v_start;
+        spp.num_seqs = cpl.V;
+        spp.min_q = 1;
+        spp.max_seqlen_k = pa->max_prefix_len;
+        spp.total_q = cpl.vtokens;
+        spp.q_rows = v_qrows;
+        spp.seq_row = v_row;
+        spp.state = state;
+        spp.q_limit = total_q;
+        spp.bt_rows = num_seqs;
+        spp.sp_tiles = (pa->max_group_size + pp.tile_tokens - 1) / pp.tile_tokens;
+
+        pkv::StateCombineParams sc{};
+        sc.prefix_states = states;
+        sc.state = state;
+        sc.state_rows = cpl.vtokens;
+        sc.num_seqs = num_seqs;
+        sc.Hq = num_q_heads;
+
+        plp.kv_start = kv_eff;
+        dp.kv_start = kv_eff;
+        pp.kv_start = kv_eff;
+        dp.prefix_states = states;
+        dp.state = state;
+        dp.state_rows = cpl.vtokens;
+        if (dtype == PKV_BF16)
+            rc = head_dim == 128 ? launch_prefix_pass<pkv::bf16_t, 128>(cp, spp, sc, cpl.max_chunks > 1, st)
+                                 : launch_prefix_pass<pkv::bf16_t, 64>(cp, spp, sc, cpl.max_chunks > 1, st);
+        else
+            rc = head_dim == 128 ? launch_prefix_pass<float, 128>(cp, spp, sc, cpl.max_chunks > 1, st)
+                                 : launch_prefix_pass<float, 64>(cp, spp, sc, cpl.max_chunks > 1, st);
+        if (rc) return rc;
+    }
+    if (dtype == PKV_BF16)
+        rc = head_dim == 128 ? launch_attention<pkv::bf16_t, 128>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
+                             : launch_attention<pkv::bf16_t, 64>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
+    else
+        rc = head_dim == 128 ? launch_attention<float, 128>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
+                             : launch_attention<float, 64>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
+    if (rc) return rc;
+    return ok();
 }
 
 }  // namespace
@@ -229,138 +529,54 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                   int64_t num_blocks, float scale, pkv_dtype_t dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {
-    if (int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype)) return rc;
-    if (num_seqs < 0) return fail(PKV_E_ARG, "num_seqs %d < 0", num_seqs);
-    if (total_q < 0) return fail(PKV_E_ARG, "total_q %lld < 0", (long long)total_q);
-    if (num_seqs == 0 || total_q == 0) return ok();
-    if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc)
-        return fail(PKV_E_ARG, "null pointer argument");
-    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-        return fail(PKV_E_ARG, "q, out and the pools must be 16-byte aligned");
-    if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "max_blocks_per_seq %d <= 0", max_blocks_per_seq);
-    if (num_blocks <= 0) return fail(PKV_E_ARG, "num_blocks %lld <= 0", (long long)num_blocks);
-    if (max_seqlen_q <= 0 || max_seqlen_k <= 0)
-        return fail(PKV_E_ARG, "max_seqlen_q %d and max_seqlen_k %d must be positive", max_seqlen_q,
-                    max_seqlen_k);
-    if (max_seqlen_q > max_seqlen_k)
-        return fail(PKV_E_ARG, "max_seqlen_q %d > max_seqlen_k %d", max_seqlen_q, max_seqlen_k);
-    if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * block_size)
-        return fail(PKV_E_ARG, "max_seqlen_k %d exceeds the block-table width (%d pages of %d)",
-                    max_seqlen_k, max_blocks_per_seq, block_size);
-    if (total_q > 0x7fffffffLL) return fail(PKV_E_ARG, "total_q too large");
-    if (!std::isfinite(scale) || !(scale > 0.f))
-        return fail(PKV_E_ARG, "scale %g is not finite and positive", (double)scale);
-    const size_t eb = elem_bytes(dtype);
-    const size_t io_bytes = (size_t)total_q * num_q_heads * head_dim * eb;
-    const size_t pool_bytes = (size_t)num_blocks * num_kv_heads * block_size * head_dim * eb;
-    if (overlaps(out, io_bytes, q, io_bytes) || overlaps(out, io_bytes, k_pool, pool_bytes) ||
-        overlaps(out, io_bytes, v_pool, pool_bytes))
-        return fail(PKV_E_ARG, "out must not alias q or the pools");
+    return attention_impl(out, q, k_pool, v_pool, block_tables, seq_lens, query_start_loc,
+                          kv_start, num_seqs, total_q, max_blocks_per_seq, max_seqlen_q,
+                          max_seqlen_k, num_q_heads, num_kv_heads, head_dim, block_size,
+                          num_blocks, scale, dtype, workspace, workspace_bytes, stream, nullptr);
+}
 
-    if (num_seqs > pkv::kMaxDecodeSeqs)
-        return fail(PKV_E_UNSUPPORTED, "num_seqs %d > %d is not supported", num_seqs,
-                    pkv::kMaxDecodeSeqs);
-    const int G = num_q_heads / num_kv_heads;
-    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, G, max_seqlen_q);
-    if (!workspace || workspace_bytes < pl.total)
-        return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                    workspace ? workspace_bytes : (size_t)0, pl.total);
-    if (!aligned16(workspace)) return fail(PKV_E_ARG, "workspace must be 16-byte aligned");
-    if (overlaps(workspace, pl.total, out, io_bytes))
-        return fail(PKV_E_ARG, "workspace must not alias out");
-    const float scale_log2 = scale * 1.4426950408889634f;
-    char* wsb = static_cast<char*>(workspace);
-    int32_t* prefix = reinterpret_cast<int32_t*>(wsb + pl.off_prefix);
-    int32_t* pbegin = reinterpret_cast<int32_t*>(wsb + pl.off_pbegin);
-    pkv::Portion* portions = reinterpret_cast<pkv::Portion*>(wsb + pl.off_portions);
-    float* ws_o = reinterpret_cast<float*>(wsb + pl.off_o);
-    float* ws_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
+size_t pkv_attention_shared_prefix_workspace_size(int num_seqs, int64_t total_q, int max_seqlen_q,
+                                                  int max_seqlen_k, int num_q_heads,
+                                                  int num_kv_heads, int head_dim, int block_size,
+                                                  pkv_dtype_t dtype, int num_groups,
+                                                  int max_group_size, int max_prefix_len) {
+    const size_t base = pkv_attention_workspace_size(num_seqs, total_q, max_seqlen_q, max_seqlen_k,
+                                                     num_q_heads, num_kv_heads, head_dim,
+                                                     block_size, dtype);
+    if (base == 0 || num_groups <= 0 || max_group_size <= 0 || max_prefix_len <= 0) return base;
+    return make_cascade_plan(base, num_seqs, num_groups, max_group_size, max_prefix_len,
+                             num_q_heads, num_kv_heads, head_dim).total;
+}
 
-    pkv::PlanParams plp;
-    plp.seq_lens = seq_lens;
-    plp.qsl = query_start_loc;
-    plp.kv_start = kv_start;
-    plp.num_seqs = num_seqs;
-    plp.Hkv = num_kv_heads;
-    plp.max_seqlen_k = max_seqlen_k;
-    plp.max_blocks = max_blocks_per_seq;
-    plp.wmax = pl.wmax;
-    plp.total_q = total_q;
-    plp.pair_prefix = prefix;
-    plp.portion_begin = pbegin;
-    plp.portions = portions;
-
-    pkv::DecodeParams dp;
-    dp.out = out;
-    dp.q = q;
-    dp.k_pool = k_pool;
-    dp.v_pool = v_pool;
-    dp.block_tables = block_tables;
-    dp.portion_begin = pbegin;
-    dp.portions = portions;
-    dp.ws_o = ws_o;
-    dp.ws_ml = ws_ml;
-    dp.max_blocks = max_blocks_per_seq;
-    dp.Hq = num_q_heads;
-    dp.Hkv = num_kv_heads;
-    dp.G = G;
-    dp.gmagic = (65536 + G - 1) / G;
-    dp.ncol = G * pl.wmax;
-    dp.num_blocks = num_blocks;
-    dp.inline_plan = num_seqs <= pkv::kInlinePlanSeqs ? 1 : 0;
-    dp.seq_lens = seq_lens;
-    dp.qsl = query_start_loc;
-    dp.kv_start = kv_start;
-    dp.num_seqs = num_seqs;
-    dp.max_seqlen_k = max_seqlen_k;
-    dp.wmax = pl.wmax;
-    dp.total_q = total_q;
-    dp.pair_prefix = prefix;
-    dp.scale_log2 = scale_log2;
-
-    pkv::MergeParams mp;
-    mp.out = out;
-    mp.ws_o = ws_o;
-    mp.ws_ml = ws_ml;
-    mp.pair_prefix = prefix;
-    mp.qsl = query_start_loc;
-    mp.num_seqs = num_seqs;
-    mp.Hq = num_q_heads;
-    mp.Hkv = num_kv_heads;
-    mp.G = G;
-    mp.ncol = G * pl.wmax;
-
-    pkv::PrefillParams pp;
-    pp.out = out;
-    pp.q = q;
-    pp.k_pool = k_pool;
-    pp.v_pool = v_pool;
-    pp.block_tables = block_tables;
-    pp.seq_lens = seq_lens;
-    pp.qsl = query_start_loc;
-    pp.kv_start = kv_start;
-    pp.num_seqs = num_seqs;
-    pp.max_blocks = max_blocks_per_seq;
-    pp.Hq = num_q_heads;
-    pp.Hkv = num_kv_heads;
-    pp.G = G;
-    pp.tile_tokens = pl.prefill_tile_tokens;
-    pp.min_q = pl.wmax + 1;
-    pp.max_seqlen_k = max_seqlen_k;
-    pp.total_q = total_q;
-    pp.num_blocks = num_blocks;
-    pp.scale_log2 = scale_log2;
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int rc;
-    if (dtype == PKV_BF16)
-        rc = head_dim == 128 ? launch_attention<pkv::bf16_t, 128>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
-                             : launch_attention<pkv::bf16_t, 64>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
-    else
-        rc = head_dim == 128 ? launch_attention<float, 128>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
-                             : launch_attention<float, 64>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);
-    if (rc) return rc;
-    return ok();
+int pkv_attention_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                const int32_t* query_start_loc, const int32_t* prefix_group,
+                                const int32_t* prefix_len, int num_groups, int max_group_size,
+                                int max_prefix_len, int num_seqs, int64_t total_q,
+                                int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int64_t num_blocks, float scale, pkv_dtype_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_groups < 0) return fail(PKV_E_ARG, "num_groups %d < 0", num_groups);
+    if (num_groups > pkv::kCascadeMaxGroups)
+        return fail(PKV_E_UNSUPPORTED, "num_groups %d > %d is not supported", num_groups,
+                    pkv::kCascadeMaxGroups);
+    PrefixArgs pa{prefix_group, prefix_len, num_groups, max_group_size, max_prefix_len};
+    if (num_groups > 0 && num_seqs > 0 && total_q > 0) {
+        if (!prefix_group || !prefix_len) return fail(PKV_E_ARG, "null pointer argument");
+        if (max_group_size <= 0)
+            return fail(PKV_E_ARG, "max_group_size %d must be positive", max_group_size);
+        if (max_prefix_len <= 0 || max_prefix_len % block_size)
+            return fail(PKV_E_ARG, "max_prefix_len %d must be a positive multiple of block_size %d",
+                        max_prefix_len, block_size);
+        if (max_prefix_len >= max_seqlen_k)
+            return fail(PKV_E_ARG, "max_prefix_len %d must be below max_seqlen_k %d",
+                        max_prefix_len, max_seqlen_k);
+    }
+    return attention_impl(out, q, k_pool, v_pool, block_tables, seq_lens, query_start_loc,
+                          nullptr, num_seqs, total_q, max_blocks_per_seq, max_seqlen_q,
+                          max_seqlen_k, num_q_heads, num_kv_heads, head_dim, block_size,
+                          num_blocks, scale, dtype, workspace, workspace_bytes, stream, &pa);
 }
 
 int pkv_check_metadata(const int32_t* block_tables, const int32_t* seq_lens,
@@ -397,6 +613,50 @@ int pkv_check_metadata(const int32_t* block_tables, const int32_t* seq_lens,
                 return fail(PKV_E_METADATA, "block_tables[%d][%lld] = %d outside [0, %lld)", s,
                             (long long)pg, b, (long long)num_blocks);
         }
+    }
+    return ok();
+}
+
+int pkv_check_shared_prefix(const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, const int32_t* prefix_group,
+                            const int32_t* prefix_len, int num_seqs, int num_groups,
+                            int max_blocks_per_seq, int block_size, int max_prefix_len) {
+    if (num_seqs < 0 || num_groups < 0 || max_blocks_per_seq < 0 || block_size <= 0)
+        return fail(PKV_E_ARG, "invalid sizes");
+    if (num_seqs == 0 || num_groups == 0) return ok();
+    if (!block_tables || !seq_lens || !query_start_loc || !prefix_group || !prefix_len)
+        return fail(PKV_E_ARG, "null pointer argument");
+    std::vector<int> first(num_groups, -1);
+    for (int g = 0; g < num_groups; ++g) {
+        const int P = prefix_len[g];
+        if (P < 0 || P % block_size || P > max_prefix_len)
+            return fail(PKV_E_METADATA, "prefix_len[%d] = %d is not a multiple of %d in [0, %d]", g,
+                        P, block_size, max_prefix_len);
+        if (P / block_size > max_blocks_per_seq)
+            return fail(PKV_E_METADATA, "prefix_len[%d] = %d exceeds the block-table width", g, P);
+    }
+    for (int s = 0; s < num_seqs; ++s) {
+        const int g = prefix_group[s];
+        if (g == -1) continue;
+        if (g < 0 || g >= num_groups)
+            return fail(PKV_E_METADATA, "prefix_group[%d] = %d outside [-1, %d)", s, g, num_groups);
+        const int n = query_start_loc[s + 1] - query_start_loc[s];
+        if (n != 1)
+            return fail(PKV_E_METADATA, "sequence %d of group %d has %d query tokens, not 1", s, g, n);
+        if (seq_lens[s] <= prefix_len[g])
+            return fail(PKV_E_METADATA, "sequence %d has %d keys, not more than its prefix of %d",
+                        s, seq_lens[s], prefix_len[g]);
+        if (first[g] < 0) {
+            first[g] = s;
+            continue;
+        }
+        const int32_t* a = block_tables + (int64_t)first[g] * max_blocks_per_seq;
+        const int32_t* b = block_tables + (int64_t)s * max_blocks_per_seq;
+        for (int pg = 0; pg < prefix_len[g] / block_size; ++pg)
+            if (a[pg] != b[pg])
+                return fail(PKV_E_METADATA,
+                            "sequences %d and %d of group %d differ at prefix page %d (%d, %d)",
+                            first[g], s, g, pg, a[pg], b[pg]);
     }
     return ok();
 }

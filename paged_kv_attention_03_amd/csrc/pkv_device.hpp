@@ -21,6 +21,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kPage = 16;  // tokens per KV page (block_size)
 
+// Floats per (token, query head) softmax state of a shared-prefix pass:
+// unnormalised output [D], running max (log2 units of the scaled logits), sum,
+// and two of padding (rows stay 16-byte aligned).
+template <int D>
+constexpr int kStateStride = D + 4;
+
 struct bf16_t {};  // tag type for bfloat16 storage (raw 16-bit patterns)
 
 template <typename T> struct Elem;

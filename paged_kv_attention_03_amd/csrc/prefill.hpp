@@ -61,6 +61,19 @@ struct PrefillParams {
     int64_t total_q;
     int64_t num_blocks;
     float scale_log2;
+    // Shared-prefix (state) pass; all null for a plain step.  With `state`
+    // set, the step's sequences are chunks of shared prefixes: every token of
+    // a sequence sees all of its keys [kv_start, seq_len) (no causal cap), its
+    // query row is q_rows[token] (< q_limit), its block-table row is
+    // seq_row[s] (< bt_rows), and each (token, head) writes its softmax state
+    // -- unnormalised output [D], running max (log2 units), sum -- to
+    // state[(token * Hq + head) * kStateStride] instead of an output row.
+    const int32_t* q_rows;
+    const int32_t* seq_row;
+    float* state;
+    int64_t q_limit;
+    int bt_rows;
+    int sp_tiles;  // state pass: tiles per sequence (grid = num_seqs x sp_tiles x Hkv)
 };
 
 constexpr int kPrefillRowBlocks = 4;                 // 32-row blocks per workgroup
@@ -234,29 +247,46 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     const int BQ = p.tile_tokens;
 
     // ---- which sequence owns this tile: largest s with qsl[s]/BQ + s <= bid
+    // (the state pass: sp_tiles tiles per sequence, in order)
+    const bool SP = p.state != nullptr;  // shared-prefix state pass
     int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.qsl[mid] / BQ + mid <= bid) lo = mid; else hi = mid - 1;
+    if (SP) {
+        lo = bid / p.sp_tiles;
+        if (lo >= p.num_seqs) return;
+    } else {
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.qsl[mid] / BQ + mid <= bid) lo = mid; else hi = mid - 1;
+        }
     }
     const int s = lo;
     int q0 = p.qsl[s];
     int n = p.qsl[s + 1] - q0;
-    if (q0 < 0 || q0 >= p.total_q || n < p.min_q || n < 2) return;
+    if (q0 < 0 || q0 >= p.total_q || n < (SP ? 1 : max(2, p.min_q))) return;
     if (n > p.total_q - q0) n = (int)(p.total_q - q0);
-    const int qt = bid - (q0 / BQ + s);
+    const int qt = SP ? bid - s * p.sp_tiles : bid - (q0 / BQ + s);
     const int tok0 = qt * BQ;
     if (qt < 0 || tok0 >= n) return;
     const int ntok = min(BQ, n - tok0);
 
     const SeqRange r = seq_range(p.seq_lens, p.kv_start, s, p.max_seqlen_k, p.max_blocks);
-    const int pos_min = r.L - n + tok0;           // position of the tile's first token
-    const int pos_max = pos_min + ntok - 1;       // ... and of its last
+    // position of the tile's first token and of its last (the state pass: every
+    // token sits past the last key)
+    const int pos_min = SP ? r.L - 1 : r.L - n + tok0;
+    const int pos_max = SP ? r.L - 1 : pos_min + ntok - 1;
     if (pos_max < r.a ||
         (!LONG && 2 * ((pos_max / kPage - r.first_page + 2) / 2) > kPrefillIdTable)) {
-        // every row sees no key (only with metadata outside the contract): write zeros
+        // every row sees no key (only with metadata outside the contract): write
+        // zeros, or the empty state
         for (int rr = tid; rr < ntok * p.G; rr += blockDim.x) {
             const int tok = rr / p.G, hh = rr % p.G;
+            if (SP) {
+                float* sr = p.state + ((int64_t)(q0 + tok0 + tok) * p.Hq + g * p.G + hh) * kStateStride<D>;
+                for (int d = 0; d < D; ++d) sr[d] = 0.f;
+                sr[D] = -INFINITY;
+                sr[D + 1] = 0.f;
+                continue;
+            }
             uint8_t* orow = static_cast<uint8_t*>(p.out) +
                             ((int64_t)(q0 + tok0 + tok) * p.Hq + g * p.G + hh) * Gm::RB;
             for (int c = 0; c < Gm::CPR; ++c) st16(orow + c * 16, u32x4{0, 0, 0, 0});
@@ -279,9 +309,15 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
         const int row = rblk * 32 + nt * 16 + col;
         const int tok = row / p.G, hh = row - (row / p.G) * p.G;
         rvalid[nt] = tok < ntok;
-        pos[nt] = rvalid[nt] ? pos_min + tok : -1;
+        pos[nt] = rvalid[nt] ? (SP ? pos_max : pos_min + tok) : -1;
         orow_idx[nt] = (int64_t)(q0 + tok0 + (rvalid[nt] ? tok : 0)) * p.Hq + g * p.G + hh;
-        const uint8_t* qrow = static_cast<const uint8_t*>(p.q) + orow_idx[nt] * Gm::RB;
+        int64_t qidx = orow_idx[nt];
+        if (SP) {  // the state pass reads the query row of the token's sequence
+            int64_t qt = p.q_rows[q0 + tok0 + (rvalid[nt] ? tok : 0)];
+            qt = (qt >= 0 && qt < p.q_limit) ? qt : 0;
+            qidx = qt * p.Hq + g * p.G + hh;
+        }
+        const uint8_t* qrow = static_cast<const uint8_t*>(p.q) + qidx * Gm::RB;
 #pragma unroll
         for (int i = 0; i < Gm::KCH; ++i) {
             u32x4 v = ld16(qrow + i * 64 + grp * 16);
@@ -321,11 +357,16 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     constexpr bool kOnePage = NW % (2 * BPP) == 0;
     const int pw = (wave / BPP) & 1;  // kOnePage: the page this wavefront loads
     typedef __attribute__((address_space(4))) const int32_t cint32_t;
+    int bts = s;  // block-table row of the sequence
+    if (SP) {
+        bts = p.seq_row[s];
+        bts = (bts >= 0 && bts < p.bt_rows) ? bts : 0;
+    }
     const cint32_t* bt_row =
-        (const cint32_t*)(p.block_tables + (int64_t)s * p.max_blocks + first_page);
+        (const cint32_t*)(p.block_tables + (int64_t)bts * p.max_blocks + first_page);
     if constexpr (!LONG) {
         for (int i = tid; i < 2 * nstage; i += blockDim.x) {
-            const int id = p.block_tables[(int64_t)s * p.max_blocks + first_page + min(i, npages - 1)];
+            const int id = p.block_tables[(int64_t)bts * p.max_blocks + first_page + min(i, npages - 1)];
             const int64_t b = (id >= 0 && id < p.num_blocks) ? id : 0;
             lds_bid[(i & 1) * kIdRow + (i >> 1)] = (uint32_t)((b * p.Hkv + g) * (Gm::PAGE / 256));
         }
@@ -519,14 +560,17 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             grow |= mt * p.scale_log2 > m_thr[nt];
         }
         if (__any(grow)) {
-            // exact column maxima, then rescale what was accumulated so far
+            // exact column maxima, then rescale what was accumulated so far in
+            // the columns that passed their threshold (the others keep their
+            // state bit for bit, so a row's result never depends on its
+            // neighbours in the tile)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 float mt = sv[nt][0];
 #pragma unroll
                 for (int t = 1; t < 8; ++t) mt = fmaxf(mt, sv[nt][t]);
                 mt = col_max(mt) * p.scale_log2;
-                const float m_new = fmaxf(m_run[nt], mt);
+                const float m_new = mt > m_thr[nt] ? fmaxf(m_run[nt], mt) : m_run[nt];
                 const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
                 const float alpha = fast_exp2(m_run[nt] - m_use);
                 m_run[nt] = m_new;
@@ -717,6 +761,7 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             const float a0 = fast_exp2(m_run[nt] - Mu);
             const float a1 = fast_exp2(m1 - Mu);
             l_tot[nt] = a0 * l_tot[nt] + a1 * l1;
+            m_run[nt] = M;  // the combined state is relative to M
 #pragma unroll
             for (int t = 0; t < Gm::NT; ++t)
 #pragma unroll
@@ -728,6 +773,18 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         if (!rvalid[nt]) continue;
+        if (SP) {
+            // the softmax state of the row, unnormalised
+            float* sr = p.state + orow_idx[nt] * kStateStride<D>;
+#pragma unroll
+            for (int t = 0; t < Gm::NT; ++t)
+                *reinterpret_cast<f32x4*>(sr + t * 16 + grp * 4) = acc[nt][t];
+            if (grp == 0) {
+                sr[D] = m_run[nt];
+                sr[D + 1] = l_tot[nt];
+            }
+            continue;
+        }
         const float inv = l_tot[nt] > 0.f ? 1.f / l_tot[nt] : 0.f;
         uint8_t* orow = static_cast<uint8_t*>(p.out) + orow_idx[nt] * Gm::RB;
 #pragma unroll

@@ -177,3 +177,81 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         pkv.pkv_append(x, x, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
                        torch.zeros(4, dtype=torch.int64))
+
+
+# ------------------------------------------------------- shared-prefix steps
+
+def _sp(lib, **over):
+    a = dict(out=FAKE, q=FAKE + 0x10000000, k=FAKE + 0x20000000, v=FAKE + 0x30000000, bt=FAKE,
+             sl=FAKE, qsl=FAKE, pg=FAKE, pl=FAKE, ng=1, mgs=4, mpl=64, num_seqs=4, total_q=4,
+             max_blocks=8, msq=1, msk=100, hq=8, hkv=2, d=128, bs=16, nb=64, scale=0.125,
+             dtype=pkv.PKV_BF16, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return lib.pkv_attention_shared_prefix(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["qsl"], a["pg"], a["pl"], a["ng"],
+        a["mgs"], a["mpl"], a["num_seqs"], a["total_q"], a["max_blocks"], a["msq"], a["msk"],
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ng=-1), pkv.PKV_E_ARG),
+    (dict(ng=1025), pkv.PKV_E_UNSUPPORTED),
+    (dict(pg=None), pkv.PKV_E_ARG),
+    (dict(pl=None), pkv.PKV_E_ARG),
+    (dict(mgs=0), pkv.PKV_E_ARG),
+    (dict(mpl=0), pkv.PKV_E_ARG),
+    (dict(mpl=40), pkv.PKV_E_ARG),             # not a multiple of the page size
+    (dict(mpl=112), pkv.PKV_E_ARG),            # not below max_seqlen_k
+    (dict(d=96), pkv.PKV_E_UNSUPPORTED),       # checked as for pkv_attention
+    (dict(scale=0.0), pkv.PKV_E_ARG),
+    (dict(), pkv.PKV_E_WORKSPACE),
+])
+def test_shared_prefix_rejects_invalid_arguments(lib, over, code):
+    assert _sp(lib, **over) == code
+    assert pkv.pkv_last_error() != ""
+
+
+def test_shared_prefix_workspace(lib):
+    plain = lib.pkv_attention_workspace_size(16, 16, 1, 4700, 40, 8, 128, 16, pkv.PKV_BF16)
+    sp = lambda ng, mgs, mpl: lib.pkv_attention_shared_prefix_workspace_size(
+        16, 16, 1, 4700, 40, 8, 128, 16, pkv.PKV_BF16, ng, mgs, mpl)
+    assert sp(0, 16, 512) == plain                # no groups: the plain plan
+    assert plain < sp(1, 16, 512) < sp(1, 16, 4096) <= sp(2, 16, 4096)  # chunks widen with groups
+    assert sp(1, 16, 512) % 256 == 0
+    need = lib.pkv_attention_shared_prefix_workspace_size(4, 4, 1, 100, 8, 2, 128, 16,
+                                                          pkv.PKV_BF16, 1, 4, 64)
+    assert _sp(lib, ws=FAKE + 0x40000000, ws_bytes=need - 1) == pkv.PKV_E_WORKSPACE
+    assert _sp(lib, ng=0, num_seqs=0) == pkv.PKV_OK     # empty step
+
+
+def _groups_step():
+    # sequences 0, 2, 3 share 2 pages (32 keys) as group 0; sequence 1 is plain
+    bt = np.array([[5, 6, 7, -1], [1, 2, -1, -1], [5, 6, 9, 10], [5, 6, 11, -1]], np.int32)
+    lens = np.array([40, 30, 60, 33], np.int32)
+    qsl = np.array([0, 1, 4, 5, 6], np.int32)
+    grp = np.array([0, -1, 0, 0], np.int32)
+    plen = np.array([32], np.int32)
+    return bt, lens, qsl, grp, plen
+
+
+def test_shared_prefix_checker_accepts_a_valid_step():
+    bt, lens, qsl, grp, plen = _groups_step()
+    pkv.pkv_check_shared_prefix(bt, lens, qsl, grp, plen, 16, 32)
+
+
+@pytest.mark.parametrize("mutate", [
+    lambda bt, lens, qsl, grp, plen: grp.__setitem__(1, 0),        # 3-token member
+    lambda bt, lens, qsl, grp, plen: grp.__setitem__(0, 1),        # group out of range
+    lambda bt, lens, qsl, grp, plen: grp.__setitem__(0, -2),
+    lambda bt, lens, qsl, grp, plen: lens.__setitem__(3, 32),      # no keys past the prefix
+    lambda bt, lens, qsl, grp, plen: bt.__setitem__((2, 1), 8),    # prefix page differs
+    lambda bt, lens, qsl, grp, plen: plen.__setitem__(0, 24),      # not whole pages
+    lambda bt, lens, qsl, grp, plen: plen.__setitem__(0, 48),      # above max_prefix_len
+])
+def test_shared_prefix_checker_rejects_bad_groups(mutate):
+    bt, lens, qsl, grp, plen = _groups_step()
+    mutate(bt, lens, qsl, grp, plen)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_check_shared_prefix(bt, lens, qsl, grp, plen, 16, 32)
+    assert e.value.code == pkv.PKV_E_METADATA
