@@ -462,19 +462,29 @@ def split_parts(steps: int, warmup: int):
     return res
 
 
-def agent_loop(run):
+def agent_loop(run, shared_prefix: int = 0):
     """The agent loop's 70 steps back to back (append one token per
-    sequence, then attention): wall time and attention time per step."""
+    sequence, then attention): wall time and attention time per step.  With
+    ``shared_prefix`` every sequence is a member of one prefix group of that
+    many keys and attention goes through pkv_attention_shared_prefix."""
     b = run.base
     kp, vp = b.new_pool("cuda", poison=False)
     kf, vf, sf = run.prefill_rows("cuda")
     pkv.pkv_append(kf, vf, kp, vp, sf)
     del kf, vf, sf
     msk = max(run.prompt) + run.steps
-    need = pkv.pkv_attention_workspace_size(b.num_seqs, b.num_seqs, 1, msk, b.num_q_heads,
-                                            b.num_kv_heads, b.head_dim, 16, b.dtype)
+    S = b.num_seqs
+    if shared_prefix:
+        need = pkv.pkv_attention_shared_prefix_workspace_size(
+            S, S, 1, msk, b.num_q_heads, b.num_kv_heads, b.head_dim, 16, b.dtype, num_groups=1,
+            max_group_size=S, max_prefix_len=shared_prefix)
+    else:
+        need = pkv.pkv_attention_workspace_size(S, S, 1, msk, b.num_q_heads, b.num_kv_heads,
+                                                b.head_dim, 16, b.dtype)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    qsl = torch.arange(b.num_seqs + 1, dtype=torch.int32, device="cuda")
+    qsl = torch.arange(S + 1, dtype=torch.int32, device="cuda")
+    group = torch.zeros(S, dtype=torch.int32, device="cuda")
+    plen = torch.tensor([shared_prefix], dtype=torch.int32, device="cuda")
     steps = []
     for i in range(run.steps):
         pos, slots, bt, sl = run.step(i)
@@ -488,8 +498,14 @@ def agent_loop(run):
             pkv.pkv_append(kn, vn, kp, vp, sl_)
             if ev is not None:
                 ev[i][0].record()
-            pkv.pkv_attention(q, kp, vp, bt, sls, qsl, b.scale, max_seqlen_q=1, max_seqlen_k=msk,
-                              out=out, workspace=ws)
+            if shared_prefix:
+                pkv.pkv_attention_shared_prefix(
+                    q, kp, vp, bt, sls, qsl, b.scale, group, plen, max_group_size=S,
+                    max_prefix_len=shared_prefix, max_seqlen_q=1, max_seqlen_k=msk, out=out,
+                    workspace=ws)
+            else:
+                pkv.pkv_attention(q, kp, vp, bt, sls, qsl, b.scale, max_seqlen_q=1,
+                                  max_seqlen_k=msk, out=out, workspace=ws)
             if ev is not None:
                 ev[i][1].record()
 
@@ -518,6 +534,14 @@ def bench_agent(k, args):
     dwall, dattn, _ = agent_loop(W.AgentRun(poison=False, duplicate_prefix=True))
     log(f"agent step {wall * 1e3:.4f} ms, attention {attn * 1e3:.4f} ms; duplicated prefix: "
         f"step {dwall * 1e3:.4f} ms, attention {dattn * 1e3:.4f} ms")
+    # the shared-prefix entry point on the same loop, and on a loop whose
+    # shared prefix is long (8192 keys) next to short private suffixes
+    swall, sattn, _ = agent_loop(W.AgentRun(poison=False), shared_prefix=512)
+    long_kw = dict(shared_prefix=8192, prompt_lens=[8192 + 256 + 48 * s for s in range(16)])
+    lwall, lattn, llog = agent_loop(W.AgentRun(poison=False, **long_kw))
+    lswall, lsattn, _ = agent_loop(W.AgentRun(poison=False, **long_kw), shared_prefix=8192)
+    log(f"shared-prefix entry point: agent attention {sattn * 1e3:.4f} ms; 8192-key prefix: "
+        f"plain {lattn * 1e3:.4f} ms, shared-prefix {lsattn * 1e3:.4f} ms")
     return {
         "metric": METRIC, "value": unique / wall / 1e9, "unit": "GB/s", "n_gpus": 1,
         "steps": run.steps, "warmup": 1, "ms_per_step": wall * 1e3, "higher_is_better": True,
@@ -533,7 +557,16 @@ def bench_agent(k, args):
                      "frac": unique / attn / 1e9 / HBM_PEAK_GBS, "traffic": None,
                      "launch_ms_mean": attn * 1e3, "algorithmic_bytes_per_launch": unique},
         "extra": {"duplicated_prefix": {"step_ms": dwall * 1e3, "attention_ms": dattn * 1e3,
-                                        "note": "same steps, prefix stored per sequence"}},
+                                        "note": "same steps, prefix stored per sequence"},
+                  "shared_prefix_entry_point": {
+                      "agent_step_ms": swall * 1e3, "agent_attention_ms": sattn * 1e3,
+                      "long_prefix": {
+                          "workload": "16 seqs, 8192-key shared prefix + 256..976 own keys, "
+                                      "70 decode steps, 40 q / 8 kv heads",
+                          "logical_kv_bytes_per_step": llog,
+                          "plain_attention_ms": lattn * 1e3, "plain_step_ms": lwall * 1e3,
+                          "shared_prefix_attention_ms": lsattn * 1e3,
+                          "shared_prefix_step_ms": lswall * 1e3}}},
     }
 
 
