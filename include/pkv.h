@@ -173,6 +173,11 @@ int pkv_attention(void *out, const void *q, const void *k_pool, const void *v_po
  * chunks, verify windows, unshared decodes) are computed as by pkv_attention.
  * kv_start is not taken (no left padding in such a step).
  *
+ * Reading a prefix once takes three more launches (group setup, prefix
+ * states, their combination), so the call pays for long prefixes shared by
+ * many sequences, whose re-reads the GPU's caches cannot absorb; for short
+ * prefixes pkv_attention is faster.
+ *
  * Host bounds: max_group_size > 0, max_prefix_len a positive multiple of
  * block_size below max_seqlen_k, 0 <= num_groups <= 1024 (num_groups == 0:
  * exactly pkv_attention).  Workspace: at least
