@@ -72,3 +72,51 @@ def test_step_replays_from_a_graph(case, monkeypatch):
         assert np.array_equal(raw_bits(out), want), f"{name}: replay {rep} differs from eager"
     assert np.array_equal(raw_bits(kp), okp.view(raw_bits(kp).dtype)), "pool bytes changed"
     log(f"graph replay: {name} ok (4 replays bitwise equal to eager)")
+
+
+@pytest.mark.gpu
+def test_shared_prefix_step_replays_from_a_graph(monkeypatch):
+    # the setup kernel hands out member slots by atomics, so replays may place
+    # members in other rows of the prefix tiles; the output must not change
+    monkeypatch.delenv("PKV_CHECK", raising=False)
+    from tests.test_gpu_shared_prefix import build
+    st = build([(512, [513 + 37 * i for i in range(16)]), (64, [65, 300])], [(200, 1), (90, 24)],
+               40, 8, 128, torch.bfloat16, 31)
+    log("graph replay: shared-prefix step")
+    q = st["q"].cuda()
+    kp, vp = st["kp"].cuda(), st["vp"].cuda()
+    bt, lens, qsl = (torch.from_numpy(st[k]).cuda() for k in ("bt", "lens", "qsl"))
+    grp, plen = torch.from_numpy(st["group"]).cuda(), torch.from_numpy(st["plen"]).cuda()
+    mq, mk = max(st["qlens"]), int(st["lens"].max())
+    need = pkv.pkv_attention_shared_prefix_workspace_size(
+        len(st["lens"]), q.shape[0], mq, mk, 40, 8, 128, 16, torch.bfloat16, num_groups=2,
+        max_group_size=16, max_prefix_len=512)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def call(out):
+        pkv.pkv_attention_shared_prefix(q, kp, vp, bt, lens, qsl, st["scale"], grp, plen,
+                                        max_group_size=16, max_prefix_len=512, max_seqlen_q=mq,
+                                        max_seqlen_k=mk, out=out, workspace=ws)
+
+    eager = torch.empty_like(q)
+    call(eager)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out)
+    torch.cuda.synchronize()
+    want = raw_bits(eager)
+    for rep in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(raw_bits(out), want), f"replay {rep} differs from eager"
+    log("graph replay: shared-prefix step ok")

@@ -113,6 +113,11 @@ CASES = [
      torch.bfloat16, 3),
     ("g16-bf16-d64", [(1024, [1025 + 100 * i for i in range(5)])], [], 16, 1, 64, torch.bfloat16,
      8),
+    # 600 sequences: the plan kernel splits the decode pass
+    ("600-seqs-plan-kernel", [(256, [257 + 7 * (i % 40) for i in range(120)]),
+                              (64, [65 + 11 * (i % 30) for i in range(100)]),
+                              (1024, [1025 + 13 * (i % 20) for i in range(80)])],
+     [(40 + 9 * (i % 50), 1) for i in range(300)], 16, 8, 128, torch.bfloat16, 120),
 ]
 
 
