@@ -167,10 +167,11 @@ int pkv_attention(void *out, const void *q, const void *k_pool, const void *v_po
  * Contract for a member s of group g: one query token (a decode), seq_lens[s]
  * > prefix_len[g], and its first prefix_len[g] / block_size block-table
  * entries are the group's shared pages (the same physical ids in every
- * member's row).  Members past the first max_group_size of a group (in
- * sequence order), and sequences that break the token or length condition,
- * are computed as plain sequences.  Other sequences of the step (prefill
- * chunks, verify windows, unshared decodes) are computed as by pkv_attention.
+ * member's row).  Sequences that break the token or length condition, and
+ * the members of a group beyond its first max_group_size (which ones is
+ * unspecified), are computed as plain sequences.  Other sequences of the
+ * step (prefill chunks, verify windows, unshared decodes) are computed as by
+ * pkv_attention.
  * kv_start is not taken (no left padding in such a step).
  *
  * Reading a prefix once takes three more launches (group setup, prefix

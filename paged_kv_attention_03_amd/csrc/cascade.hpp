@@ -5,18 +5,19 @@
 // The pages name the case: requests that share a prompt prefix keep it in
 // shared pages (vllm-metal v0.4.0 release post, "Prefix caching on hybrid
 // models"; the vllm-mlx paper summary, results: prefix caching measured on
-// 512-token shared prefixes).  Attention over the union of two key sets is the log-sum-exp
-// combination of the attention over each, so a step splits into
+// 512-token shared prefixes).  Attention over the union of two key sets is the
+// log-sum-exp combination of the attention over each, so a step splits into
 //   1. the prefix pass: for every group, chunk of its prefix and kv head, one
 //      matrix-core tile computes the softmax states (max, sum, unnormalised
 //      output) of all the group's query rows over that chunk -- the
 //      chunked-prefill kernel run on a virtual step whose sequences are the
 //      chunks and whose tokens are the group's decode tokens;
-//   2. the decode pass over each sequence's own keys only (kv_start = prefix
-//      length), whose first piece per segment starts from the combined
-//      prefix states; the merge of cut segments is unchanged.
-// This kernel builds the virtual step of (1) and the per-sequence inputs of
-// (2) on the device, from the caller's group arrays.
+//   2. the combination of each member's chunk states into one (below);
+//   3. the decode pass over each sequence's own keys only (kv_start = prefix
+//      length), whose first piece per segment starts from the prefix state;
+//      the merge of cut segments is unchanged.
+// The setup kernel builds the virtual step of (1) and the per-sequence inputs
+// of (2) and (3) on the device, from the caller's group arrays.
 #pragma once
 
 #include "pkv_device.hpp"
@@ -35,7 +36,7 @@ struct CascadeParams {
     const int32_t* seq_lens;      // [num_seqs]
     int num_seqs;
     int num_groups;
-    int max_members;  // members per group kept (later ones run as plain sequences)
+    int max_members;  // members per group kept (any others run as plain sequences)
     int max_chunks;   // chunks per group
     int chunk;        // keys per chunk (a multiple of 32)
     int64_t total_q;
@@ -49,16 +50,16 @@ struct CascadeParams {
     int32_t* v_qrows;       // [V * max_members] query row of each virtual token
 };
 
-// LDS the setup kernel needs for a step (dynamic: sized to the step).
-inline size_t cascade_setup_lds(int num_seqs, int num_groups) {
-    (void)num_seqs;
+// LDS the setup kernel needs for a step (dynamic: sized to the step's groups).
+inline size_t cascade_setup_lds(int num_groups) {
     return sizeof(int32_t) * (5 * (size_t)num_groups + 1 + kPlanThreads);
 }
 
-// Every sequence is handled by its own thread: a member takes a slot in its
-// group with an LDS atomic (slot order is arbitrary; the prefix pass computes
-// each query row independently of the others in its tile, so results do not
-// depend on it).
+// Sequences are spread over the threads (at most 16 each); a member takes a
+// slot in its group with an LDS atomic.  Slot order is arbitrary: the prefix
+// pass computes each query row independently of the other rows of its tile,
+// so no output bit depends on it; when a group has more members than
+// max_members, which of them run as plain sequences is unspecified.
 __global__ void __launch_bounds__(kCascadeThreads) cascade_setup_kernel(CascadeParams p) {
     extern __shared__ int32_t smem[];
     const int t = threadIdx.x;

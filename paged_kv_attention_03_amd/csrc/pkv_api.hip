@@ -224,7 +224,7 @@ template <typename T, int D>
 int launch_prefix_pass(const pkv::CascadeParams& cp, const pkv::PrefillParams& spp,
                        const pkv::StateCombineParams& sc, bool combine, hipStream_t stream) {
     hipLaunchKernelGGL(pkv::cascade_setup_kernel, dim3(1), dim3(pkv::kCascadeThreads),
-                       pkv::cascade_setup_lds(cp.num_seqs, cp.num_groups), stream, cp);
+                       pkv::cascade_setup_lds(cp.num_groups), stream, cp);
     if (int rc = hip_status("shared-prefix setup launch")) return rc;
     if (int rc = launch_prefill<T, D>(spp, stream, "shared-prefix state launch")) return rc;
     if (combine) {  // prefixes of more than one chunk
