@@ -28,6 +28,10 @@ namespace pkv {
 constexpr int kCascadeThreads = 1024;
 constexpr int kCascadeMaxSeqs = 16384;   // sequences a step may hold
 constexpr int kCascadeMaxGroups = 1024;  // groups per step
+// the entry point admits up to kMaxDecodeSeqs sequences; the setup kernel
+// must give every one of them its prefix inputs
+static_assert(kCascadeMaxSeqs >= kMaxDecodeSeqs, "setup kernel covers fewer sequences than a step");
+static_assert(kCascadeMaxSeqs % kCascadeThreads == 0, "sequences split evenly over threads");
 
 struct CascadeParams {
     const int32_t* prefix_group;  // [num_seqs]: group of sequence s, or -1
