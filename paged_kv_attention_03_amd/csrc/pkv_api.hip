@@ -218,8 +218,9 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
     return PKV_OK;
 }
 
-// Shared-prefix steps, ahead of the plain launches: the setup kernel, then
-// the prefix states of every (group, chunk, kv head) from the prefill kernel.
+// Shared-prefix steps, ahead of the plain launches: the setup kernel, the
+// prefix states of every (group, chunk, kv head) from the prefill kernel, and
+// the combination of each member's chunk states when a prefix spans chunks.
 template <typename T, int D>
 int launch_prefix_pass(const pkv::CascadeParams& cp, const pkv::PrefillParams& spp,
                        const pkv::StateCombineParams& sc, bool combine, hipStream_t stream) {
