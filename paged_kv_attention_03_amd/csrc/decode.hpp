@@ -144,6 +144,24 @@ __device__ __forceinline__ int64_t wave_of(int64_t u, int64_t U) {
     return ((u + 1) * kDecodeWaves + U - 1) / U - 1;
 }
 
+// Units are ordered kv head first: head g's segments, one per decode sequence
+// in sequence order, fill [g * P[S], (g + 1) * P[S]) where P is the exclusive
+// prefix of the sequences' page pairs.  Segment (s, g) starts at:
+__device__ __forceinline__ int64_t segment_start(int g, int32_t P_s, int32_t P_S) {
+    return (int64_t)g * P_S + P_s;
+}
+
+// Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD b % 8);
+// decode wave numbers count along each XCD instead, so that XCD x streams a
+// contiguous eighth of the units: with the head-first order, the pages of one
+// kv head (or of a contiguous run of heads).  Pages several sequences share (a
+// common prefix) are then fetched once into that XCD's L2 and re-read there.
+constexpr int kXcds = 8;
+static_assert(kDecodeWaves % kXcds == 0, "waves spread evenly over the XCDs");
+__device__ __forceinline__ int decode_wave_id() {
+    return (int)(blockIdx.x % kXcds) * (kDecodeWaves / kXcds) + (int)(blockIdx.x / kXcds);
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
     // Orders this wave's LDS writes before its later LDS reads (and the reverse)
     // without waiting on outstanding global loads.
@@ -207,17 +225,18 @@ __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(PlanParams p)
     auto walk = [&](int w, bool emit, int32_t out_at) -> int {
         const int64_t u0 = wave_start(w, U), u1 = wave_start(w + 1, U);
         if (u0 >= u1) return 0;
-        int lo = 0, hi = S - 1;  // largest s with Hkv * C[s] <= u0 (then C[s+1] > C[s])
+        int g = (int)(u0 / C[S]);
+        const int64_t r0 = u0 - (int64_t)g * C[S];
+        int lo = 0, hi = S - 1;  // largest s with C[s] <= r0 (then C[s+1] > C[s])
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)p.Hkv * C[mid] <= u0) lo = mid; else hi = mid - 1;
+            if (C[mid] <= r0) lo = mid; else hi = mid - 1;
         }
         int s = lo;
         int64_t c = C[s + 1] - C[s];
-        int g = (int)((u0 - (int64_t)p.Hkv * C[s]) / c);
         int count = 0;
         while (true) {
-            const int64_t seg0 = (int64_t)p.Hkv * C[s] + (int64_t)g * c;
+            const int64_t seg0 = segment_start(g, C[s], C[S]);
             const int64_t seg1 = seg0 + c;
             if (emit) {
                 Portion q;
@@ -235,11 +254,14 @@ __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(PlanParams p)
             }
             ++count;
             if (seg1 >= u1) break;
-            if (++g == p.Hkv) {
-                g = 0;
-                do { ++s; } while (C[s + 1] == C[s]);
-                c = C[s + 1] - C[s];
+            // next segment: the next sequence with pairs, else the next head's first
+            do { ++s; } while (s < S && C[s + 1] == C[s]);
+            if (s == S) {
+                ++g;
+                s = 0;
+                while (C[s + 1] == C[s]) ++s;
             }
+            c = C[s + 1] - C[s];
         }
         return count;
     };
@@ -286,7 +308,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int w = blockIdx.x;
+    const int w = decode_wave_id();
     const bool inl = p.inline_plan != 0;
     const int S = p.num_seqs;
     int pb = 0, pe = 0;       // plan-kernel mode: this wave's pieces
@@ -339,14 +361,15 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     int64_t wc = 0;
     bool wdone = !inl;
     if (inl) {
-        int lo = 0, hi = S - 1;  // largest s with Hkv * P[s] <= u0 (then P[s+1] > P[s])
+        wg = (int)(u0 / pref(S));
+        const int64_t r0 = u0 - (int64_t)wg * pref(S);
+        int lo = 0, hi = S - 1;  // largest s with P[s] <= r0 (then P[s+1] > P[s])
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)p.Hkv * pref(mid) <= u0) lo = mid; else hi = mid - 1;
+            if (pref(mid) <= r0) lo = mid; else hi = mid - 1;
         }
         ws = lo;
         wc = pref(ws + 1) - pref(ws);
-        wg = (int)((u0 - (int64_t)p.Hkv * pref(ws)) / wc);
     }
 
     const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
@@ -381,7 +404,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
         } else {
             if (wdone) break;
             while (n < kWave && !wdone) {
-                const int64_t seg0 = (int64_t)p.Hkv * pref(ws) + (int64_t)wg * wc;
+                const int64_t seg0 = segment_start(wg, pref(ws), pref(S));
                 const int64_t seg1 = seg0 + wc;
                 Portion q;
                 q.s = ws;
@@ -400,9 +423,13 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                 ++wcount;
                 if (seg1 >= u1) {
                     wdone = true;
-                } else if (++wg == p.Hkv) {
-                    wg = 0;
-                    do { ++ws; } while (pref(ws + 1) == pref(ws));
+                } else {
+                    do { ++ws; } while (ws < S && pref(ws + 1) == pref(ws));
+                    if (ws == S) {
+                        ++wg;
+                        ws = 0;
+                        while (pref(ws + 1) == pref(ws)) ++ws;
+                    }
                     wc = pref(ws + 1) - pref(ws);
                 }
             }
@@ -743,7 +770,7 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeParams p) {
     if (c <= 0) return;
     const int64_t U = (int64_t)p.Hkv * p.pair_prefix[p.num_seqs];
     const int g = h / p.G, head = h - (h / p.G) * p.G;
-    const int64_t a = (int64_t)p.Hkv * p.pair_prefix[s] + g * c;
+    const int64_t a = segment_start(g, p.pair_prefix[s], p.pair_prefix[p.num_seqs]);
     const int64_t wa = wave_of(a, U), wb = wave_of(a + c - 1, U);
     if (wa == wb) return;  // the wave that holds the whole segment wrote it
     const int lane = threadIdx.x;
