@@ -10,10 +10,13 @@
 //
 // Work split (split-key, balanced): a one-workgroup plan kernel counts the
 // page pairs of every decode sequence and cuts the list of all
-// (sequence, kv head, page pair) units into kDecodeWaves equal contiguous
+// (kv head, sequence, page pair) units into kDecodeWaves equal contiguous
 // ranges.  One persistent wavefront streams each range, crossing from one
 // (sequence, kv head) segment to the next without leaving the kernel, so every
-// wave does the same number of page pairs whatever the length mix.  A segment
+// wave does the same number of page pairs whatever the length mix.  Wave
+// numbers count along each XCD, so an XCD streams one kv head's pages (or a
+// contiguous run of heads) and pages shared by several sequences are re-read
+// from its L2.  A segment
 // that lies inside one wave's range is finished there and written to the
 // output; a segment cut by a range boundary leaves at most two partial results
 // per wave, which a small merge kernel combines with the usual log-sum-exp
@@ -313,7 +316,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     const int S = p.num_seqs;
     int pb = 0, pe = 0;       // plan-kernel mode: this wave's pieces
     int64_t u0 = 0, u1 = 0;   // inline mode: this wave's units [u0, u1)
-    int64_t units = 0;        // (sequence, kv head, page pair) units of the step
+    int64_t units = 0;        // (kv head, sequence, page pair) units of the step
     if (inl) {
         // page pairs of every sequence and their exclusive prefix, in LDS
         const int per = (S + kWave - 1) / kWave;
