@@ -62,3 +62,38 @@ def test_random_step(seed):
     out = gpu_attention(st, q.cuda(), kp, vp)
     ref = oracle_step(st, q, pools=(okp, ovp))
     check_close(out, ref, st.dtype, f"random step {seed}")
+
+
+# Decode units are ordered kv head first and cut over waves numbered along the
+# XCDs; head counts that do not divide the 8 XCDs put head boundaries inside
+# an XCD's share and segments across XCD boundaries.
+KV_HEAD_CASES = [
+    # (kv heads, group size, sequences, with windows and a chunk)
+    (3, 2, 40, True),
+    (5, 1, 30, True),
+    (12, 2, 20, True),
+    (7, 3, 9, False),
+    (3, 1, 600, False),  # above 512 sequences: the plan kernel cuts the work
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", KV_HEAD_CASES, ids=[f"hkv{c[0]}-g{c[1]}-s{c[2]}" for c in KV_HEAD_CASES])
+def test_kv_head_counts_that_do_not_divide_the_xcds(case):
+    hkv, G, S, mixed = case
+    rng = np.random.default_rng(77 + hkv * 100 + S)
+    lens = [int(x) for x in rng.integers(1, 700 if S < 100 else 200, size=S)]
+    ql = [1] * S
+    if mixed:
+        for i in range(0, S, 7):
+            ql[i] = min(lens[i], max(2, 16 // G))  # verify windows
+        lens[1] = max(lens[1], 400)
+        ql[1] = 150  # one prefill chunk
+    log(f"kv heads {hkv}, G {G}, {S} sequences, mixed {mixed}")
+    st = W.build_step(f"hkv{hkv}-s{S}", lens, ql, G * hkv, hkv, 128, torch.bfloat16, 8100 + hkv)
+    q = st.make_q("cpu")
+    kp, vp = gpu_pools(st, "cpu")
+    okp, ovp = oracle_pools(st)
+    out = gpu_attention(st, q.cuda(), kp, vp)
+    ref = oracle_step(st, q, pools=(okp, ovp))
+    check_close(out, ref, st.dtype, f"kv heads {hkv}, {S} sequences")
