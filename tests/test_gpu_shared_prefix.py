@@ -139,7 +139,7 @@ def test_shared_prefix_step_matches_the_oracle(case):
 @pytest.mark.gpu
 def test_members_breaking_the_contract_run_as_plain_sequences():
     # in group 0: a 2-token window and a sequence with no keys past the prefix;
-    # the checker rejects the step, the kernels compute both as plain sequences
+    # pkv_check_shared_prefix rejects the step; the kernels compute both as plain sequences
     st = build([(128, [129, (300, 2), 128, 200]), (32, [33, 90])], [(500, 1)], 16, 4, 128,
                torch.bfloat16, 77)
     with pytest.raises(pkv.PkvError):
