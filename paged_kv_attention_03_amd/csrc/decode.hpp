@@ -56,13 +56,19 @@ constexpr int kMaxDecodeSeqs = 16384;  // sequences the plan kernel can hold in 
 constexpr int kWindowPages = 256;      // block-table entries staged per window
 constexpr int kInlinePlanSeqs = 512;   // up to this many sequences each decode wave
                                        // plans its own pieces (no plan kernel)
-// Steps whose decode K/V exceed this many bytes (twice the 256 MB Infinity
-// Cache) stream them with non-temporal loads: read once, they would only
-// displace each other from the caches, and the hint lifts the read rate of a
-// pure stream by ~10% on MI355X (measured: 7.0 against 6.4 TB/s).  Smaller
-// steps keep cacheable loads, which let repeated pages (a shared prefix, the
-// next step's contexts) hit the Infinity Cache.
-constexpr int64_t kStreamBytes = 512ll << 20;
+// Decode K/V are read with non-temporal loads.  Within a call every page of a
+// (sequence, kv head) is read once, and a page several sequences share is
+// re-read from the XCD's L2 shortly after its first read, which the hint
+// leaves intact (an 8192-key prefix shared by 16 decodes: 0.0770 against
+// 0.0768 ms with cacheable loads).  Across calls, a model with many layers
+// reads every other layer's K/V and weights between two calls of one layer,
+// so nothing of the previous call is left in the 256 MB Infinity Cache to
+// reuse; the hint then only keeps streamed pages from displacing each other.
+// Measured on MI355X with the caches cleared before each call: a pure stream
+// 7.0 against 6.4 TB/s, the 16-sequence decode step 0.041 against 0.042-0.044
+// ms, the mixed chunked-prefill step 0.153 against 0.160 ms.  Only a loop that
+// re-runs one layer's call back to back loses (the 16-sequence agent loop:
+// 0.056 against 0.052 ms), as its previous call's pages no longer stay cached.
 
 // A wave's piece of one (sequence, kv head) segment: page pairs [pi0, pi1).
 struct Portion {
@@ -316,7 +322,6 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
     const int S = p.num_seqs;
     int pb = 0, pe = 0;       // plan-kernel mode: this wave's pieces
     int64_t u0 = 0, u1 = 0;   // inline mode: this wave's units [u0, u1)
-    int64_t units = 0;        // (kv head, sequence, page pair) units of the step
     if (inl) {
         // page pairs of every sequence and their exclusive prefix, in LDS
         const int per = (S + kWave - 1) / kWave;
@@ -348,15 +353,11 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
         u0 = wave_start(w, U);
         u1 = wave_start(w + 1, U);
         if (u0 >= u1) return;
-        units = U;
     } else {
         pb = p.portion_begin[w];
         pe = p.portion_begin[w + 1];
         if (pb >= pe) return;
-        units = (int64_t)p.Hkv * p.pair_prefix[S];
     }
-    // a unit is one page pair of one kv head: K and V of two pages
-    const bool stream_nt = units * 4 * kPage * Gm::RB > kStreamBytes;
     auto pref = [&](int s) { return __builtin_amdgcn_readfirstlane(lds_pref[s]); };
     // inline mode: the walk over the segments that meet [u0, u1) -- sequence
     // ws, kv head wg, ws's pairs wc, pieces emitted so far
@@ -472,13 +473,10 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                 wseq = is;
             }
             const int64_t head_off = (int64_t)ig * kPage * Gm::RB;
-            // The same loads in both arms (same registers): only the cache hint
-            // differs.  A pair issued past the cursor's end (never consumed) and
-            // the second page of a pair that has one page in range use empty
-            // resources: the loads return zeros without touching memory, which
-            // matters once they are not cache hits.
-            auto load_pair = [&](auto nt_tag) {
-                constexpr bool NT = decltype(nt_tag)::value;
+            // A pair issued past the cursor's end (never consumed) and the
+            // second page of a pair that has one page in range use empty
+            // resources: the loads return zeros without touching memory.
+            {
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int pg = x ? pb2 : pa;
@@ -488,14 +486,12 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
                     const auto vr = buffer_rsrc(vpool + blk * page_stride + head_off, bytes);
 #pragma unroll
                     for (int i = 0; i < Gm::KCH; ++i)
-                        R.k[x][i] = buffer_ld16<NT>(kr, col * Gm::RB + i * 64 + grp * 16);
+                        R.k[x][i] = buffer_ld16<true>(kr, col * Gm::RB + i * 64 + grp * 16);
 #pragma unroll
                     for (int c = 0; c < Gm::VCH; ++c)
-                        R.v[x][c] = buffer_ld16<NT>(vr, (c * kWave + lane) * 16);
+                        R.v[x][c] = buffer_ld16<true>(vr, (c * kWave + lane) * 16);
                 }
-            };
-            if (stream_nt) load_pair(std::true_type{});
-            else load_pair(std::false_type{});
+            }
             // advance; past the end the last pair is issued again (zeros, unused)
             if (!idone && ++ipi == iend) {
                 if (ip + 1 < n) {

@@ -67,9 +67,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 // 16-byte buffer load at byte offset off; NT sets the non-temporal hint (the
-// data is streamed past the caches instead of displacing reused lines).  The
-// hint is an immediate of the instruction, so code that picks it at run time
-// keeps two loads the compiler cannot merge.
+// data is streamed past the caches instead of displacing reused lines), an
+// immediate of the instruction.
 template <bool NT>
 __device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
