@@ -152,14 +152,14 @@ int oracle_attention(double *out, const void *q, const void *k_pool, const void 
     const int D = head_dim;
     const int64_t units = (int64_t)num_seqs * num_kv_heads;
     int failed = 0;
+    /* num_threads > 0 limits this call only; 0 uses the OpenMP default */
 #ifdef _OPENMP
-    if (num_threads > 0)
-        omp_set_num_threads(num_threads);
+    const int nthr = num_threads > 0 ? num_threads : omp_get_max_threads();
 #else
     (void)num_threads;
 #endif
 
-#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#pragma omp parallel for num_threads(nthr) schedule(dynamic, 1) reduction(| : failed)
     for (int64_t u = 0; u < units; ++u) {
         const int s = (int)(u / num_kv_heads);
         const int g = (int)(u % num_kv_heads);

@@ -236,7 +236,9 @@ def test_thread_count_invariance_bitwise(oracle_lib):
     st = _step(SMALL_CASES[2])
     q = st.make_q("cpu")
     pools = oracle_pools(st)
+    before = oracle.max_threads()
     assert np.array_equal(oracle_step(st, q, pools, threads=1), oracle_step(st, q, pools, threads=8))
+    assert oracle.max_threads() == before  # a thread limit applies to its own call only
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -252,28 +254,49 @@ def test_left_padded_equals_ragged_bitwise(dtype, oracle_lib):
     assert np.array_equal(a, b)
 
 
+def _agent_layout(run, share, seed):
+    """Block tables and slots of an agent run laid out in a shuffled pool of
+    the test's own: with ``share`` the prefix pages are listed by every
+    sequence, else each sequence holds its own copy of the prefix."""
+    rng = np.random.default_rng(seed)
+    S, P = run.num_seqs, run.shared_prefix
+    npg = [(n + 15) // 16 for n in run.final_lens]
+    nb = sum(npg) + 8
+    free = list(rng.permutation(nb))
+    shared = [int(free.pop()) for _ in range(P // 16)] if share else []
+    bt = np.full((S, max(npg)), -1, np.int32)
+    slots = []
+    for s in range(S):
+        for p in range(npg[s]):
+            bt[s, p] = shared[p] if p < len(shared) else int(free.pop())
+        j = np.arange(run.final_lens[s], dtype=np.int64)
+        slots.append(bt[s, j // 16].astype(np.int64) * 16 + j % 16)
+    return bt, slots, nb
+
+
 def test_shared_prefix_equals_duplicated_prefix_bitwise(oracle_lib):
-    common = dict(steps=3, num_q_heads=4, num_kv_heads=2, head_dim=16,
-                  prompt_lens=[40, 57, 33, 64], shared_prefix=32)
-    sh = W.AgentRun(**common)
-    du = W.AgentRun(duplicate_prefix=True, **common)
-    assert len(sh.shared_pages) == 2
-    assert all((sh.block_tables[s, :2] == sh.shared_pages).all() for s in range(4))
-    assert len(set(du.block_tables[:, 0].tolist())) == 4
-    for run in (sh, du):
-        kp, vp = run.base.new_pool("cpu")
-        k, v, s = run.prefill_rows("cpu")
-        run._pools = list(oracle.oracle_append(kp, vp, k, v, s))
-    for i in range(3):
-        outs = []
-        for run in (sh, du):
-            pos, slots, bt, sl = run.step(i)
-            k, v = run.step_rows(i, "cpu")
-            run._pools = list(oracle.oracle_append(run._pools[0], run._pools[1], k, v, slots))
-            q = run.step_q(i, "cpu")
-            outs.append(oracle.oracle_attention(q, run._pools[0], run._pools[1], bt, sl,
-                                                np.arange(5, dtype=np.int32), run.base.scale))
-        assert np.array_equal(outs[0], outs[1])
+    run = W.AgentRun(steps=3, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                     prompt_lens=[40, 57, 33, 64], shared_prefix=32)
+    rows = [run.seq_kv(s, "cpu") for s in range(run.num_seqs)]
+    outs = []
+    for share in (True, False):
+        bt, slots, nb = _agent_layout(run, share, 5)
+        if share:
+            assert all((bt[s, :2] == bt[0, :2]).all() for s in range(4))
+        else:
+            assert len(set(bt[:, 0].tolist())) == 4
+        kp = torch.full((nb, 2, 16, 16), float("nan"), dtype=run.dtype)
+        vp = kp.clone()
+        for s, (k, v) in enumerate(rows):  # a shared page is written with identical rows
+            kp, vp = oracle.oracle_append(kp, vp, k, v, slots[s])
+        res = []
+        for i in range(run.steps):
+            res.append(oracle.oracle_attention(run.step_q(i, "cpu"), kp, vp, bt,
+                                               run.seq_lens_at(i), np.arange(5, dtype=np.int32),
+                                               run.scale))
+        outs.append(res)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
 
 
 def test_poisoned_pool_never_reaches_the_result(oracle_lib):
