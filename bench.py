@@ -232,10 +232,91 @@ def cpu_baseline(st, budget_s: float = 10.0):
     e = 2 if st.dtype == torch.bfloat16 else 4
     kvb = covered * 2 * st.num_kv_heads * st.head_dim * e
     return {"value": kvb / med / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "tokens_per_s": seqs / med,
+            "kind": "oracle", "tokens_per_s": seqs / med, "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(), "small_configs": oracle_small_configs(),
             "sample": f"first {seqs} of {st.num_seqs} sequences ({covered} keys, "
                       f"{kvb / 1e9:.2f} GB of K/V); median of {len(passes)} passes, "
                       f"{spent:.1f} s of oracle time"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_small_configs(reps: int = 3):
+    """The oracle on the tiny decode step (config 1) and the 16-sequence
+    decode step (config 2), whole step, with all host threads and with one:
+    median of ``reps`` calls (page gather + math; inputs prepared before)."""
+    import oracle
+    res = {}
+    for k in (1, 2):
+        st = W.config_step(k, poison=False)
+        q = st.make_q("cpu")
+        kp, vp = st.new_pool("cpu")
+        for which in ("fill", "step"):
+            kr, vr, sl = st.rows(which, "cpu")
+            kp, vp = oracle.oracle_append(kp, vp, kr, vr, sl)
+        md = st.metadata("cpu")
+        args = (q, kp, vp, md["block_tables"], md["seq_lens"], md["query_start_loc"], st.scale)
+        e = 2 if st.dtype == torch.bfloat16 else 4
+        kvb = sum(st.real_lens) * 2 * st.num_kv_heads * st.head_dim * e
+        rec = {"workload": st.name, "kv_bytes": kvb}
+        for name, th in (("all_threads", 0), ("one_thread", 1)):
+            ts = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                oracle.oracle_attention(*args, threads=th)
+                ts.append(time.perf_counter() - t0)
+            t = float(np.median(ts))
+            rec[name] = {"ms": t * 1e3, "tokens_per_s": st.total_q / t, "kv_gbs": kvb / t / 1e9,
+                         "threads": oracle.max_threads() if th == 0 else 1}
+        res[st.name] = rec
+    return res
+
+
+def launch_latency(reps: int = 50):
+    """The tiny decode step (config 1: 4 sequences, 214 keys, fp32): a step
+    whose bytes take nanoseconds, so its time is launch latency.  Per rep:
+    the attention call's device time (HIP events around it on the launch
+    stream), the host time to enqueue it through the binding, and the wall
+    time of append + attention + synchronize.  Median and min over ``reps``."""
+    st = W.config_step(1, poison=False)
+    step = Step(st, gen_device="cuda")
+    for _ in range(10):
+        step.append()
+        step.attention()
+    torch.cuda.synchronize()
+    dev, host, wall = [], [], []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        step.append()
+        a.record()
+        t1 = time.perf_counter()
+        step.attention()
+        t2 = time.perf_counter()
+        b.record()
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        dev.append(a.elapsed_time(b) * 1e3)
+        host.append((t2 - t1) * 1e6)
+        wall.append((t3 - t0) * 1e6)
+    del step
+    torch.cuda.empty_cache()
+    stat = lambda xs: {"median": float(np.median(xs)), "min": float(np.min(xs))}
+    return {"workload": st.name, "reps": reps, "unit": "us",
+            "attention_device_us": stat(dev), "attention_enqueue_host_us": stat(host),
+            "step_wall_us": stat(wall),
+            "note": "device: HIP events around the attention call (decode + merge kernels); "
+                    "host: the binding's enqueue of that call; wall: append + attention + "
+                    "synchronize"}
 
 
 def extra_prefill(steps: int, warmup: int):
@@ -330,7 +411,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
@@ -349,6 +430,14 @@ def main():
               flush=True)
         return
     k = args.config
+    if k == 1:
+        lat = launch_latency(max(args.steps, 20))
+        print(json.dumps({"metric": "launch latency of the tiny decode step", "unit": "us",
+                          "value": lat["step_wall_us"]["median"], "higher_is_better": False,
+                          "n_gpus": 1, "steps": lat["reps"], "warmup": 10, "dtype": "f32",
+                          "data": "synthetic N(0,1), seeded", "config": {"workload": lat["workload"]},
+                          "detail": lat}), flush=True)
+        return
     if k == 4:
         run_main = bench_agent
     else:
@@ -399,6 +488,7 @@ def bench_single(k, args):
         rec["extra"] = extra_prefill(min(args.steps, 20), args.warmup)
         rec["extra"]["verify_windows"] = extra_windows(min(args.steps, 20), args.warmup)
         rec["extra"]["pool_manager"] = extra_pool()
+        rec["extra"]["launch_latency"] = launch_latency()
     if not args.no_extra and k == 3:
         rec["extra"] = {"split_parts": split_parts(min(args.steps, 20), args.warmup)}
     if not args.no_cpu_baseline:
@@ -462,96 +552,87 @@ def split_parts(steps: int, warmup: int):
     return res
 
 
-def agent_loop(run, shared_prefix: int = 0):
-    """The agent loop's 70 steps back to back (append one token per
-    sequence, then attention): wall time and attention time per step.  With
-    ``shared_prefix`` every sequence is a member of one prefix group of that
-    many keys and attention goes through pkv_attention_shared_prefix."""
-    b = run.base
-    kp, vp = b.new_pool("cuda", poison=False)
-    kf, vf, sf = run.prefill_rows("cuda")
-    pkv.pkv_append(kf, vf, kp, vp, sf)
-    del kf, vf, sf
-    msk = max(run.prompt) + run.steps
-    S = b.num_seqs
-    if shared_prefix:
-        need = pkv.pkv_attention_shared_prefix_workspace_size(
-            S, S, 1, msk, b.num_q_heads, b.num_kv_heads, b.head_dim, 16, b.dtype, num_groups=1,
-            max_group_size=S, max_prefix_len=shared_prefix)
-    else:
-        need = pkv.pkv_attention_workspace_size(S, S, 1, msk, b.num_q_heads, b.num_kv_heads,
-                                                b.head_dim, 16, b.dtype)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    qsl = torch.arange(S + 1, dtype=torch.int32, device="cuda")
-    group = torch.zeros(S, dtype=torch.int32, device="cuda")
-    plen = torch.tensor([shared_prefix], dtype=torch.int32, device="cuda")
-    steps = []
+def agent_loop(run, share_prefix: bool = True, prefix_pass=None):
+    """The agent loop as an engine runs it: each of the 70 steps plans its
+    metadata on the host (pool manager: one slot per sequence, copy-on-write
+    check, block-table export), uploads it, appends one token per sequence
+    and attends.  A first loop warms up (a fresh pool each time, the manager
+    being stateful).  Returns wall time per step (host planning included),
+    attention time per step (HIP events on the launch stream), the logical
+    K/V bytes per step and the host planning time per step."""
+    from paged_kv_attention_03_amd.engine import AgentLoop, AgentPlanner
+
+    def make():
+        planner = AgentPlanner(run, share_prefix=share_prefix)
+        return AgentLoop(run, planner, poison=False, gen_device="cuda", prefix_pass=prefix_pass)
+
+    lp = make()
     for i in range(run.steps):
-        pos, slots, bt, sl = run.step(i)
-        kn, vn = run.step_rows(i, "cuda")
-        steps.append((kn, vn, torch.from_numpy(slots).cuda(), torch.from_numpy(bt).cuda(),
-                      torch.tensor(sl, dtype=torch.int32, device="cuda"), run.step_q(i, "cuda"), sl))
-    out = torch.empty_like(steps[0][5])
-
-    def loop(ev=None):
-        for i, (kn, vn, sl_, bt, sls, q, _) in enumerate(steps):
-            pkv.pkv_append(kn, vn, kp, vp, sl_)
-            if ev is not None:
-                ev[i][0].record()
-            if shared_prefix:
-                pkv.pkv_attention_shared_prefix(
-                    q, kp, vp, bt, sls, qsl, b.scale, group, plen, max_group_size=S,
-                    max_prefix_len=shared_prefix, max_seqlen_q=1, max_seqlen_k=msk, out=out,
-                    workspace=ws)
-            else:
-                pkv.pkv_attention(q, kp, vp, bt, sls, qsl, b.scale, max_seqlen_q=1,
-                                  max_seqlen_k=msk, out=out, workspace=ws)
-            if ev is not None:
-                ev[i][1].record()
-
-    loop()
+        lp.step(i)
     torch.cuda.synchronize()
+    lp.plan.close()
+    del lp
+    lp = make()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in steps]
-    t0 = time.perf_counter()
-    loop(ev)
+          for _ in range(run.steps)]
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / len(steps)
+    t0 = time.perf_counter()
+    for i in range(run.steps):
+        lp.step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / run.steps
     attn = float(np.mean([a.elapsed_time(c) for a, c in ev])) / 1e3
-    logical = sum(sum(s[6]) for s in steps) * 2 * b.num_kv_heads * b.head_dim * 2 / len(steps)
-    del kp, vp, steps, ws, out
+    lp.plan.close()
+    del lp
     torch.cuda.empty_cache()
-    return wall, attn, logical
+    # host planning alone, on a fresh manager (no device work)
+    planner = AgentPlanner(run, share_prefix=share_prefix)
+    planner.prefill()
+    t0 = time.perf_counter()
+    for i in range(run.steps):
+        planner.step(i)
+    host = (time.perf_counter() - t0) / run.steps
+    planner.close()
+    logical = float(np.mean([sum(run.seq_lens_at(i)) for i in range(run.steps)])) * \
+        2 * run.num_kv_heads * run.head_dim * 2
+    return wall, attn, logical, host
 
 
 def bench_agent(k, args):
-    run = W.AgentRun(poison=False)
-    b = run.base
-    wall, attn, logical = agent_loop(run)
-    unique = logical - (b.num_seqs - 1) * 512 * 2 * b.num_kv_heads * b.head_dim * 2
+    run = W.AgentRun()
+    wall, attn, logical, host = agent_loop(run)
+    unique = logical - (run.num_seqs - 1) * run.shared_prefix * 2 * run.num_kv_heads * \
+        run.head_dim * 2
     # the same loop with the prefix stored once per sequence: what the shared
-    # pages save through the caches as it is (the bound on a cascade pass)
-    dwall, dattn, _ = agent_loop(W.AgentRun(poison=False, duplicate_prefix=True))
-    log(f"agent step {wall * 1e3:.4f} ms, attention {attn * 1e3:.4f} ms; duplicated prefix: "
-        f"step {dwall * 1e3:.4f} ms, attention {dattn * 1e3:.4f} ms")
-    # the shared-prefix entry point on the same loop, and on a loop whose
-    # shared prefix is long (8192 keys) next to short private suffixes
-    swall, sattn, _ = agent_loop(W.AgentRun(poison=False), shared_prefix=512)
+    # pages save through the caches as it is (the bound on a prefix pass)
+    dwall, dattn, _, _ = agent_loop(W.AgentRun(), share_prefix=False)
+    log(f"agent step {wall * 1e3:.4f} ms (host planning {host * 1e6:.1f} us), attention "
+        f"{attn * 1e3:.4f} ms; duplicated prefix: step {dwall * 1e3:.4f} ms, attention "
+        f"{dattn * 1e3:.4f} ms")
+    # the shared-prefix entry point on the same loop (routed by the library,
+    # and with the prefix pass forced), and on a loop whose shared prefix is
+    # long (8192 keys) next to short private suffixes
+    _, sattn, _, _ = agent_loop(W.AgentRun(), prefix_pass="auto")
+    _, fattn, _, _ = agent_loop(W.AgentRun(), prefix_pass="always")
     long_kw = dict(shared_prefix=8192, prompt_lens=[8192 + 256 + 48 * s for s in range(16)])
-    lwall, lattn, llog = agent_loop(W.AgentRun(poison=False, **long_kw))
-    lswall, lsattn, _ = agent_loop(W.AgentRun(poison=False, **long_kw), shared_prefix=8192)
-    log(f"shared-prefix entry point: agent attention {sattn * 1e3:.4f} ms; 8192-key prefix: "
-        f"plain {lattn * 1e3:.4f} ms, shared-prefix {lsattn * 1e3:.4f} ms")
+    lwall, lattn, llog, _ = agent_loop(W.AgentRun(**long_kw))
+    lswall, lsattn, _, _ = agent_loop(W.AgentRun(**long_kw), prefix_pass="auto")
+    log(f"shared-prefix entry point: agent attention {sattn * 1e3:.4f} ms (auto), "
+        f"{fattn * 1e3:.4f} ms (prefix pass forced); 8192-key prefix: plain {lattn * 1e3:.4f} ms, "
+        f"shared-prefix (auto) {lsattn * 1e3:.4f} ms")
     return {
         "metric": METRIC, "value": unique / wall / 1e9, "unit": "GB/s", "n_gpus": 1,
-        "steps": run.steps, "warmup": 1, "ms_per_step": wall * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic N(0,1), seeded; 512-token prefix in shared pages",
-        "config": {"workload": b.name, "num_seqs": b.num_seqs, "decode_steps": run.steps,
-                   "q_heads": b.num_q_heads, "kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
-                   "page_size": 16, "logical_kv_bytes_per_step": logical,
-                   "unique_kv_bytes_per_step": unique},
-        "packed_step_tokens_per_s": b.num_seqs / wall,
+        "steps": run.steps, "warmup": run.steps, "ms_per_step": wall * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0,1), seeded; 512-token prefix in shared pages; pages from the "
+                "host pool manager (shuffled free list)",
+        "config": {"workload": run.name, "num_seqs": run.num_seqs, "decode_steps": run.steps,
+                   "q_heads": run.num_q_heads, "kv_heads": run.num_kv_heads,
+                   "head_dim": run.head_dim, "page_size": 16, "logical_kv_bytes_per_step": logical,
+                   "unique_kv_bytes_per_step": unique,
+                   "step": "host planning (pool manager) + metadata upload + append + attention"},
+        "packed_step_tokens_per_s": run.num_seqs / wall,
+        "host_planning_us_per_step": host * 1e6,
         "roofline": {"bound": "hbm", "kernel": "decode pass (decode_kernel + merge_kernel)",
                      "achieved": unique / attn / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": unique / attn / 1e9 / HBM_PEAK_GBS, "traffic": None,
@@ -559,14 +640,15 @@ def bench_agent(k, args):
         "extra": {"duplicated_prefix": {"step_ms": dwall * 1e3, "attention_ms": dattn * 1e3,
                                         "note": "same steps, prefix stored per sequence"},
                   "shared_prefix_entry_point": {
-                      "agent_step_ms": swall * 1e3, "agent_attention_ms": sattn * 1e3,
+                      "agent_attention_ms_auto": sattn * 1e3,
+                      "agent_attention_ms_prefix_pass_forced": fattn * 1e3,
                       "long_prefix": {
                           "workload": "16 seqs, 8192-key shared prefix + 256..976 own keys, "
                                       "70 decode steps, 40 q / 8 kv heads",
                           "logical_kv_bytes_per_step": llog,
                           "plain_attention_ms": lattn * 1e3, "plain_step_ms": lwall * 1e3,
-                          "shared_prefix_attention_ms": lsattn * 1e3,
-                          "shared_prefix_step_ms": lswall * 1e3}}},
+                          "shared_prefix_attention_ms_auto": lsattn * 1e3,
+                          "shared_prefix_step_ms_auto": lswall * 1e3}}},
     }
 
 

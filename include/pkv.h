@@ -76,9 +76,9 @@ enum {
  * For every token t with slot_mapping[t] >= 0, copies k_new[t][h][:] to
  * k_pool[slot / block_size][h][slot % block_size][:] for every kv head h, and
  * the same for v.  A pure byte copy: the pool is updated in place, never
- * copied as a whole (vllm-metal v0.4.0 release post, "Prefix caching on hybrid
- * models": rows are written in place instead of copying the pool; "Replacing
- * attention, reusing the rest": admitted requests grow without reshaping).
+ * copied as a whole (vllm-metal v0.4.0 release post, "Replacing attention,
+ * reusing the rest": KV stays in fixed-size pages located by per-request
+ * block tables, so admitted requests grow without reshaping a cache).
  *
  * slot_mapping entries must be unique among non-negative values and lie in
  * [0, num_blocks * block_size); a slot outside that range is skipped.  Pages
@@ -109,9 +109,14 @@ size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqle
  * the token sees (see the header comment), K_j and V_j read from kv head
  * h / (num_q_heads / num_kv_heads) of the page block_tables[s][j / block_size]
  * at offset j % block_size.  Pages may be shared by several sequences (a common
- * prefix); they are only read.  Bytes of the pool outside the visible keys,
- * including the rest of a sequence's last page and pages below kv_start, are
- * never allowed to reach the output, whatever they hold (NaN included).
+ * prefix); they are only read.  Bytes of the pool outside a sequence's keys
+ * [kv_start, seq_len) -- the rest of its last page, pages below kv_start,
+ * free pages -- never reach the output, whatever they hold (NaN included).
+ * The keys inside that range are the sequence's own rows and must be finite:
+ * the tokens of one chunk or window share each key's value row in one
+ * matrix product, so a non-finite value in a later token's row of the same
+ * chunk or window would turn the earlier tokens' outputs (which give it zero
+ * weight) into NaN.
  * (vllm-metal v0.4.0 release post, "Replacing attention, reusing the rest";
  * left padding with masked leading keys: vllm-ios README, "How it works" and
  * "What this is and isn't".)
@@ -175,16 +180,25 @@ int pkv_attention(void *out, const void *q, const void *k_pool, const void *v_po
  * kv_start is not taken (no left padding in such a step).
  *
  * Reading a prefix once takes three more launches (group setup, prefix
- * states, their combination), so the call pays for long prefixes shared by
- * many sequences, whose re-reads the GPU's caches cannot absorb; for short
- * prefixes pkv_attention is faster.
+ * states, their combination), so the prefix pass pays for long prefixes
+ * shared by many sequences, whose re-reads the GPU's caches cannot absorb;
+ * for short prefixes the plain path is faster.  prefix_pass selects:
+ *   PKV_PREFIX_PASS_AUTO (0): the library runs the prefix pass only when the
+ *     prefix re-reads it can avoid, estimated from the host bounds as
+ *     num_groups * (min(max_group_size, num_seqs) - 1) * max_prefix_len keys
+ *     of K and V, reach 256 MiB; otherwise the step runs exactly as
+ *     pkv_attention (the group arrays are then not read).
+ *   PKV_PREFIX_PASS_ALWAYS (1): always run the prefix pass.
  *
  * Host bounds: max_group_size > 0, max_prefix_len a positive multiple of
  * block_size below max_seqlen_k, 0 <= num_groups <= 1024 (num_groups == 0:
  * exactly pkv_attention).  Workspace: at least
- * pkv_attention_shared_prefix_workspace_size(...) bytes with the same bounds.
- * Errors and every other argument as for pkv_attention.
+ * pkv_attention_shared_prefix_workspace_size(...) bytes with the same bounds
+ * (whichever path runs).  Errors and every other argument as for
+ * pkv_attention.
  */
+enum { PKV_PREFIX_PASS_AUTO = 0, PKV_PREFIX_PASS_ALWAYS = 1 };
+
 size_t pkv_attention_shared_prefix_workspace_size(int num_seqs, int64_t total_q, int max_seqlen_q,
                                                   int max_seqlen_k, int num_q_heads,
                                                   int num_kv_heads, int head_dim, int block_size,
@@ -199,20 +213,25 @@ int pkv_attention_shared_prefix(void *out, const void *q, const void *k_pool, co
                                 int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                 int64_t num_blocks, float scale, pkv_dtype_t dtype,
-                                void *workspace, size_t workspace_bytes, void *stream);
+                                int prefix_pass, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 /*
  * pkv_check_metadata -- validate HOST copies of the step metadata against the
  * contract above: query_start_loc starts at 0, is non-decreasing and ends at
  * total_q; 0 <= kv_start[s] <= seq_lens[s]; each sequence's query count is at
- * most seq_lens[s] - kv_start[s]; every page a visible key lives on is listed
- * and lies in [0, num_blocks).  Returns PKV_OK or PKV_E_METADATA (reason in
- * pkv_last_error()).  kv_start may be NULL.
+ * most seq_lens[s] - kv_start[s] and at most max_seqlen_q; seq_lens[s] is at
+ * most max_seqlen_k; every page a visible key lives on is listed and lies in
+ * [0, num_blocks).  max_seqlen_q and max_seqlen_k are the host bounds that
+ * will be passed to pkv_attention: a step that exceeds them would leave output
+ * rows unwritten (too many query tokens) or lose keys (too long a sequence),
+ * so both are checked.  Returns PKV_OK, PKV_E_METADATA (reason in
+ * pkv_last_error()) or PKV_E_ARG for invalid sizes.  kv_start may be NULL.
  */
 int pkv_check_metadata(const int32_t *block_tables, const int32_t *seq_lens,
                        const int32_t *query_start_loc, const int32_t *kv_start, int num_seqs,
-                       int64_t total_q, int max_blocks_per_seq, int block_size,
-                       int64_t num_blocks);
+                       int64_t total_q, int max_blocks_per_seq, int max_seqlen_q,
+                       int max_seqlen_k, int block_size, int64_t num_blocks);
 
 /*
  * pkv_check_shared_prefix -- validate HOST copies of a shared-prefix step's
@@ -249,8 +268,8 @@ const char *pkv_last_error(void);
  * common prefix hold the same physical pages (reference counts); a sequence
  * about to write into a page it shares first moves to a private copy of that
  * page (copy-on-write), so pages shared by several sequences are only read,
- * as pkv_append requires ("Prefix caching on hybrid models": rows are written
- * in place).  The manager produces slot_mapping, block-table rows and
+ * as pkv_append requires ("Prefix caching on hybrid models": reusing a
+ * prefix goes through the paged path's block tables).  The manager produces slot_mapping, block-table rows and
  * seq_lens for the device calls above; it never touches device memory itself
  * (pkv_copy_blocks performs the page copies it asks for).  All pointers of
  * pkv_pool_* are HOST pointers.  A pool is not thread-safe: one host thread
@@ -264,6 +283,12 @@ typedef struct pkv_pool pkv_pool_t;
 pkv_pool_t *pkv_pool_create(int64_t num_blocks, int block_size, int max_seqs,
                             int max_blocks_per_seq);
 void pkv_pool_destroy(pkv_pool_t *pool);
+
+/* Sets the order in which the free pages are handed out (order[0] first):
+ * order must list each of the n == pkv_pool_free_blocks() free pages once,
+ * else PKV_E_ARG and nothing changes.  A pool that has served for a while
+ * hands out pages in no particular order; this reproduces any placement. */
+int pkv_pool_set_free_order(pkv_pool_t *pool, const int32_t *order, int64_t n);
 
 /* Free pages, and whether a new sequence of num_tokens tokens fits now
  * (1 / 0; -1 for a NULL pool). */

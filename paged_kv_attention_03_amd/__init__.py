@@ -41,6 +41,9 @@ PKV_E_WORKSPACE = -3
 PKV_E_HIP = -4
 PKV_E_METADATA = -5
 PKV_E_NOMEM = -6
+PKV_PREFIX_PASS_AUTO = 0
+PKV_PREFIX_PASS_ALWAYS = 1
+_PREFIX_PASS = {"auto": PKV_PREFIX_PASS_AUTO, "always": PKV_PREFIX_PASS_ALWAYS}
 
 _lib = None
 
@@ -79,11 +82,11 @@ def load_library():
     lib.pkv_attention_shared_prefix_workspace_size.restype = sz
     lib.pkv_attention_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                                 i32, i64, i32, i32, i32, i32, i32, i32, i32,
-                                                i64, ctypes.c_float, i32, vp, sz, vp]
+                                                i64, ctypes.c_float, i32, i32, vp, sz, vp]
     lib.pkv_attention_shared_prefix.restype = i32
     lib.pkv_check_shared_prefix.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32]
     lib.pkv_check_shared_prefix.restype = i32
-    lib.pkv_check_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i64]
+    lib.pkv_check_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i64]
     lib.pkv_check_metadata.restype = i32
     lib.pkv_check_slots.argtypes = [vp, i64, i32, i64]
     lib.pkv_check_slots.restype = i32
@@ -95,6 +98,8 @@ def load_library():
     lib.pkv_pool_destroy.restype = None
     lib.pkv_pool_free_blocks.argtypes = [vp]
     lib.pkv_pool_free_blocks.restype = i64
+    lib.pkv_pool_set_free_order.argtypes = [vp, vp, i64]
+    lib.pkv_pool_set_free_order.restype = i32
     lib.pkv_pool_can_admit.argtypes = [vp, i64]
     lib.pkv_pool_can_admit.restype = i32
     lib.pkv_pool_add_seq.argtypes = [vp, i32]
@@ -227,7 +232,8 @@ def pkv_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
             _dev(query_start_loc, "query_start_loc", torch.int32),
             None if kv_start is None else _dev(kv_start, "kv_start", torch.int32))
     if os.environ.get("PKV_CHECK") == "1":
-        pkv_check_metadata(block_tables, seq_lens, query_start_loc, kv_start, total_q, bs, nb)
+        pkv_check_metadata(block_tables, seq_lens, query_start_loc, kv_start, total_q, bs, nb,
+                           max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
     _raise(lib.pkv_attention(*ptrs, ns, total_q, max_blocks, int(max_seqlen_q), int(max_seqlen_k),
                              hq, hkv, d, bs, nb, float(scale), dt, ws_ptr, ws_bytes,
                              _stream(q.device, stream)))
@@ -253,12 +259,16 @@ def pkv_attention_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
                                 max_group_size: int, max_prefix_len: int, max_seqlen_q: int,
                                 max_seqlen_k: int, out: Optional[torch.Tensor] = None,
                                 workspace: Optional[torch.Tensor] = None,
-                                stream=None) -> torch.Tensor:
+                                prefix_pass: str = "auto", stream=None) -> torch.Tensor:
     """pkv_attention for a step whose decode sequences share prefixes in groups:
     prefix_group [S] int32 (group or -1), prefix_len [num_groups] int32 (shared
-    keys, multiples of the page size).  Same result as pkv_attention; each
-    group's shared pages are read once per kv head."""
+    keys, multiples of the page size).  Same result as pkv_attention; with the
+    prefix pass each group's shared pages are read once per kv head.
+    ``prefix_pass``: "auto" (the library runs the pass only when the re-reads it
+    avoids are large) or "always"."""
     lib = load_library()
+    if prefix_pass not in _PREFIX_PASS:
+        raise ValueError(f"prefix_pass must be one of {sorted(_PREFIX_PASS)}")
     dt = _dtype_code(q.dtype)
     if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [total_q, Hq, D] and pools [num_blocks, Hkv, bs, D]")
@@ -292,13 +302,14 @@ def pkv_attention_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
             _dev(prefix_group, "prefix_group", torch.int32),
             _dev(prefix_len, "prefix_len", torch.int32))
     if os.environ.get("PKV_CHECK") == "1":
-        pkv_check_metadata(block_tables, seq_lens, query_start_loc, None, total_q, bs, nb)
+        pkv_check_metadata(block_tables, seq_lens, query_start_loc, None, total_q, bs, nb,
+                           max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
         pkv_check_shared_prefix(block_tables, seq_lens, query_start_loc, prefix_group,
                                 prefix_len, bs, max_prefix_len)
     _raise(lib.pkv_attention_shared_prefix(
         *ptrs, ng, int(max_group_size), int(max_prefix_len), ns, total_q, max_blocks,
-        int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), dt, ws_ptr,
-        ws_bytes, _stream(q.device, stream)))
+        int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), dt,
+        _PREFIX_PASS[prefix_pass], ws_ptr, ws_bytes, _stream(q.device, stream)))
     return out
 
 
@@ -326,8 +337,12 @@ def _host_i32(x):
 
 
 def pkv_check_metadata(block_tables, seq_lens, query_start_loc, kv_start, total_q: int,
-                       block_size: int, num_blocks: int) -> None:
-    """Validate host copies of the step metadata; raises PkvError."""
+                       block_size: int, num_blocks: int, *, max_seqlen_q: Optional[int] = None,
+                       max_seqlen_k: Optional[int] = None) -> None:
+    """Validate host copies of the step metadata against the host bounds that
+    pkv_attention will receive (``None``: the step's own maxima, i.e. only the
+    other rules are checked); raises PkvError."""
+    import numpy as np
     bt = _host_i32(block_tables)
     sl = _host_i32(seq_lens)
     qsl = _host_i32(query_start_loc)
@@ -335,9 +350,14 @@ def pkv_check_metadata(block_tables, seq_lens, query_start_loc, kv_start, total_
     ns = sl.shape[0]
     if bt.ndim != 2 or bt.shape[0] != ns or qsl.shape != (ns + 1,):
         raise ValueError("metadata shapes disagree")
+    if max_seqlen_q is None:
+        max_seqlen_q = int(np.max(np.diff(qsl), initial=0)) if ns else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int(np.max(sl, initial=0)) if ns else 0
     _raise(load_library().pkv_check_metadata(bt.ctypes.data, sl.ctypes.data, qsl.ctypes.data,
                                              None if ks is None else ks.ctypes.data, ns,
-                                             int(total_q), bt.shape[1], block_size, num_blocks))
+                                             int(total_q), bt.shape[1], max(int(max_seqlen_q), 0),
+                                             max(int(max_seqlen_k), 0), block_size, num_blocks))
 
 
 def pkv_check_slots(slot_mapping, block_size: int, num_blocks: int) -> None:
@@ -396,6 +416,12 @@ class PagePool:
     @property
     def free_blocks(self) -> int:
         return int(self._lib.pkv_pool_free_blocks(self._h))
+
+    def set_free_order(self, order) -> None:
+        """Hand out the free pages in this order (a permutation of them)."""
+        import numpy as np
+        o = np.ascontiguousarray(np.asarray(order, dtype=np.int32))
+        _raise(self._lib.pkv_pool_set_free_order(self._h, o.ctypes.data, o.shape[0]))
 
     def can_admit(self, num_tokens: int) -> bool:
         return self._lib.pkv_pool_can_admit(self._h, num_tokens) == 1

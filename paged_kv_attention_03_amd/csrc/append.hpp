@@ -1,8 +1,10 @@
 // Slot-mapped append of this step's K/V rows into the page pool.
 //
 // Each new token's rows are written in place into the slot its scheduler
-// chose (vllm-metal v0.4.0 release post, "Prefix caching on hybrid models":
-// rows go in place rather than through a copy of the whole pool).  One thread
+// chose: keys and values stay in fixed-size pages that per-request block
+// tables locate, so a request grows by filling its pages, never by reshaping
+// or copying a cache (vllm-metal v0.4.0 release post, "Replacing attention,
+// reusing the rest").  One thread
 // moves one 16-byte chunk of a K row and the matching chunk of the V row, so
 // the kernel reads and writes exactly the bytes of the new rows, coalesced
 // along head_dim.

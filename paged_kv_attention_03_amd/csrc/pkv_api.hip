@@ -236,6 +236,23 @@ int launch_prefix_pass(const pkv::CascadeParams& cp, const pkv::PrefillParams& s
     return PKV_OK;
 }
 
+// Whether reading each group's prefix once pays for its three extra launches
+// (setup, prefix states, combine: ~18 us measured): the K/V re-reads it
+// avoids, estimated from the host bounds, against a threshold between the two
+// measured cases on MI355X (16 decodes, 40 q / 8 kv heads): a 512-key prefix
+// (31 MB avoided; plain path 0.056 ms, prefix pass 0.072 ms) and an 8192-key
+// prefix (503 MB avoided; plain 0.075 ms, prefix pass 0.055 ms).
+constexpr double kPrefixPassMinSavedBytes = 256.0 * 1024 * 1024;
+
+bool prefix_pass_pays(int num_seqs, int num_groups, int max_group_size, int max_prefix_len,
+                      int num_kv_heads, int head_dim, pkv_dtype_t dtype) {
+    const double members = std::min(max_group_size, num_seqs);
+    if (num_groups <= 0 || members < 2) return false;
+    const double saved = (double)num_groups * (members - 1) * max_prefix_len * 2.0 *
+                         num_kv_heads * head_dim * (double)elem_bytes(dtype);
+    return saved >= kPrefixPassMinSavedBytes;
+}
+
 // Shared-prefix groups of a step (pkv_attention_shared_prefix).
 struct PrefixArgs {
     const int32_t* prefix_group;
@@ -243,6 +260,8 @@ struct PrefixArgs {
     int num_groups;
     int max_group_size;
     int max_prefix_len;
+    bool run_pass;  // false: the step runs as pkv_attention (the workspace is
+                    // still checked against the prefix pass's plan)
 };
 
 int attention_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -285,12 +304,13 @@ int attention_impl(void* out, const void* q, const void* k_pool, const void* v_p
                     pkv::kMaxDecodeSeqs);
     const int G = num_q_heads / num_kv_heads;
     const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, G, max_seqlen_q);
-    const bool cascade = pa != nullptr && pa->num_groups > 0;
+    const bool grouped = pa != nullptr && pa->num_groups > 0;
+    const bool cascade = grouped && pa->run_pass;
     CascadePlan cpl;
-    if (cascade)
+    if (grouped)
         cpl = make_cascade_plan(pl.total, num_seqs, pa->num_groups, pa->max_group_size,
                                 pa->max_prefix_len, num_q_heads, num_kv_heads, head_dim);
-    const size_t need = cascade ? cpl.total : pl.total;
+    const size_t need = grouped ? cpl.total : pl.total;
     if (!workspace || workspace_bytes < need)
         return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                     workspace ? workspace_bytes : (size_t)0, need);
@@ -557,12 +577,16 @@ int pkv_attention_shared_prefix(void* out, const void* q, const void* k_pool, co
                                 int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                 int64_t num_blocks, float scale, pkv_dtype_t dtype,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                int prefix_pass, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    // head counts, head_dim, block_size and dtype first: the prefix checks
+    // below divide by block_size
+    if (int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype)) return rc;
     if (num_groups < 0) return fail(PKV_E_ARG, "num_groups %d < 0", num_groups);
     if (num_groups > pkv::kCascadeMaxGroups)
         return fail(PKV_E_UNSUPPORTED, "num_groups %d > %d is not supported", num_groups,
                     pkv::kCascadeMaxGroups);
-    PrefixArgs pa{prefix_group, prefix_len, num_groups, max_group_size, max_prefix_len};
+    PrefixArgs pa{prefix_group, prefix_len, num_groups, max_group_size, max_prefix_len, true};
     if (num_groups > 0 && num_seqs > 0 && total_q > 0) {
         if (!prefix_group || !prefix_len) return fail(PKV_E_ARG, "null pointer argument");
         if (max_group_size <= 0)
@@ -574,6 +598,11 @@ int pkv_attention_shared_prefix(void* out, const void* q, const void* k_pool, co
             return fail(PKV_E_ARG, "max_prefix_len %d must be below max_seqlen_k %d",
                         max_prefix_len, max_seqlen_k);
     }
+    if (prefix_pass != PKV_PREFIX_PASS_AUTO && prefix_pass != PKV_PREFIX_PASS_ALWAYS)
+        return fail(PKV_E_ARG, "prefix_pass %d is neither AUTO nor ALWAYS", prefix_pass);
+    pa.run_pass = prefix_pass == PKV_PREFIX_PASS_ALWAYS ||
+                  prefix_pass_pays(num_seqs, num_groups, max_group_size, max_prefix_len,
+                                   num_kv_heads, head_dim, dtype);
     return attention_impl(out, q, k_pool, v_pool, block_tables, seq_lens, query_start_loc,
                           nullptr, num_seqs, total_q, max_blocks_per_seq, max_seqlen_q,
                           max_seqlen_k, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -582,8 +611,10 @@ int pkv_attention_shared_prefix(void* out, const void* q, const void* k_pool, co
 
 int pkv_check_metadata(const int32_t* block_tables, const int32_t* seq_lens,
                        const int32_t* query_start_loc, const int32_t* kv_start, int num_seqs,
-                       int64_t total_q, int max_blocks_per_seq, int block_size, int64_t num_blocks) {
-    if (num_seqs < 0 || block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+                       int64_t total_q, int max_blocks_per_seq, int max_seqlen_q,
+                       int max_seqlen_k, int block_size, int64_t num_blocks) {
+    if (num_seqs < 0 || block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0 ||
+        max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(PKV_E_ARG, "invalid sizes");
     if (num_seqs == 0) return ok();
     if (!block_tables || !seq_lens || !query_start_loc)
@@ -603,6 +634,12 @@ int pkv_check_metadata(const int32_t* block_tables, const int32_t* seq_lens,
         if (n > L - a)
             return fail(PKV_E_METADATA, "sequence %d has %lld query tokens but %lld visible keys", s,
                         (long long)n, (long long)(L - a));
+        if (n > max_seqlen_q)
+            return fail(PKV_E_METADATA, "sequence %d has %lld query tokens, above max_seqlen_q %d",
+                        s, (long long)n, max_seqlen_q);
+        if (L > max_seqlen_k)
+            return fail(PKV_E_METADATA, "seq_lens[%d] = %lld is above max_seqlen_k %d", s,
+                        (long long)L, max_seqlen_k);
         if (L == 0) continue;
         const int64_t last = (L - 1) / block_size;
         if (last >= max_blocks_per_seq)
@@ -710,6 +747,14 @@ void pkv_pool_destroy(pkv_pool_t* pool) { delete pool; }
 
 int64_t pkv_pool_free_blocks(const pkv_pool_t* pool) {
     return pool ? pool->pool.free_blocks() : -1;
+}
+
+int pkv_pool_set_free_order(pkv_pool_t* pool, const int32_t* order, int64_t n) {
+    if (!pool) return fail(PKV_E_ARG, "null pool");
+    if (pool->pool.set_free_order(order, n) != pkv::PagePool::kOk)
+        return fail(PKV_E_ARG, "the order must list each of the %lld free pages once",
+                    (long long)pool->pool.free_blocks());
+    return ok();
 }
 
 int pkv_pool_can_admit(const pkv_pool_t* pool, int64_t num_tokens) {

@@ -48,6 +48,23 @@ public:
     }
     const std::vector<int32_t>& pages(int seq) const { return seqs_[(size_t)seq].pages; }
 
+    // Sets the order in which the free pages are handed out: order[0] first.
+    // order must list every free page exactly once (a pool that has served
+    // requests for a while hands out pages in no particular order; a caller
+    // can reproduce that, or any placement, by a permutation of its own).
+    Status set_free_order(const int32_t* order, int64_t n) {
+        if (n != free_blocks() || (n > 0 && !order)) return kBadArg;
+        std::vector<uint8_t> seen((size_t)num_blocks_, 0);
+        for (int64_t i = 0; i < n; ++i) {
+            const int32_t b = order[i];
+            if (b < 0 || b >= num_blocks_ || ref_[(size_t)b] != 0 || seen[(size_t)b]) return kBadArg;
+            seen[(size_t)b] = 1;
+        }
+        // free_ is a stack (back = next page handed out)
+        for (int64_t i = 0; i < n; ++i) free_[(size_t)(n - 1 - i)] = order[i];
+        return kOk;
+    }
+
     // Pages a new sequence of num_tokens tokens needs now.
     int64_t pages_for(int64_t num_tokens) const { return (num_tokens + bs_ - 1) / bs_; }
     bool can_admit(int64_t num_tokens) const {

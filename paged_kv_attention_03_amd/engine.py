@@ -1,0 +1,201 @@
+"""A decode loop over a pool reserved once: the host pool manager hands out
+pages, the device calls write and read them.
+
+This is the host side of an engine step as the pages describe it: the KV pool
+is sized once at startup and every request draws its pages from it (vllm-metal
+v0.4.0 release post, "Set a predictable memory budget"); requests that share a
+prompt prefix hold it in common pages ("Prefix caching on hybrid models"); each
+step the scheduler hands the runner slots for the new rows and block tables
+("How vllm-metal fits into vLLM"), and the step appends its rows and runs
+attention through the tables ("Replacing attention, reusing the rest").
+
+``AgentPlanner`` is host only (the ``pkv_pool_*`` manager: fork for the shared
+prefix, one ``append_batch`` per step, block-table export).  ``AgentLoop``
+owns the device pools and runs each step: metadata upload, any copy-on-write
+page copies (``pkv_copy_blocks``), ``pkv_append`` of the step's rows, then
+``pkv_attention``.  Neither holds any attention arithmetic.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import PagePool, pkv_append, pkv_attention, pkv_attention_shared_prefix, \
+    pkv_attention_shared_prefix_workspace_size, pkv_attention_workspace_size, pkv_copy_blocks
+
+BLOCK_SIZE = 16
+
+
+@dataclass
+class StepPlan:
+    """Host metadata of one decode step."""
+    slots: np.ndarray                 # [S] int64, the new token's slot per sequence
+    copies: List[Tuple[int, int]]     # copy-on-write page copies to run first
+    table: np.ndarray                 # [S, width] int32 block tables (-1 past the pages)
+    lens: np.ndarray                  # [S] int32 keys per sequence, new token included
+
+
+class AgentPlanner:
+    """Pool-manager bookkeeping of the agent workload (``workloads.AgentRun``).
+
+    With ``share_prefix`` the first sequence's prompt prefix is written once
+    and every other sequence is forked from it (its prefix pages held in
+    common); otherwise every sequence holds its own copy.  The pool holds
+    ``pool_factor`` x the pages the whole run needs and hands out its free
+    pages in the run's seeded order."""
+
+    def __init__(self, run, share_prefix: bool = True, pool_factor: float = 1.25):
+        self.run = run
+        self.share = share_prefix and run.shared_prefix > 0
+        S = run.num_seqs
+        bs = BLOCK_SIZE
+        need = sum((n + bs - 1) // bs for n in run.final_lens)
+        if self.share:
+            need -= (S - 1) * (run.shared_prefix // bs)
+        self.num_blocks = int(math.ceil(pool_factor * need))
+        self.width = (run.max_seqlen_k + bs - 1) // bs
+        self.pool = PagePool(self.num_blocks, bs, S, self.width)
+        self.pool.set_free_order(run.free_order(self.num_blocks))
+        self.seqs = list(range(S))
+        self.shared_pages: List[int] = []
+
+    def prefill(self):
+        """Pages for every prompt.  Returns [(seq, lo, hi, slots)]: rows lo..hi
+        of sequence seq go to ``slots`` (the shared prefix is listed once)."""
+        run, pool = self.run, self.pool
+        P = run.shared_prefix if self.share else 0
+        segs = []
+        if self.share:
+            pool.add_seq(0)
+            slots, _ = pool.append(0, P)
+            segs.append((0, 0, P, slots))
+            for s in self.seqs[1:]:
+                pool.fork(0, s, P)
+            table, _ = pool.block_tables([0], self.width)
+            self.shared_pages = [int(b) for b in table[0][:P // BLOCK_SIZE]]
+        else:
+            for s in self.seqs:
+                pool.add_seq(s)
+        counts = [run.prompt[s] - P for s in self.seqs]
+        slots, copies = pool.append_batch(self.seqs, counts)
+        assert not copies  # the prefix fills whole pages
+        at = 0
+        for s, c in zip(self.seqs, counts):
+            segs.append((s, P, P + c, slots[at:at + c]))
+            at += c
+        return segs
+
+    def step(self, i: int) -> StepPlan:
+        """Decode step i: one new token per sequence."""
+        slots, copies = self.pool.append_batch(self.seqs, [1] * len(self.seqs))
+        table, lens = self.pool.block_tables(self.seqs, self.width)
+        return StepPlan(slots=slots, copies=copies, table=table, lens=lens)
+
+    def close(self):
+        self.pool.close()
+
+
+class AgentLoop:
+    """The agent workload on the device, driven by an :class:`AgentPlanner`.
+
+    Every row the run will append is generated on ``gen_device`` up front (the
+    model's projections would produce them; they are inputs), so a step's
+    device work is the upload of its metadata, the append and attention.
+    Pool bytes no row was written to hold NaN when ``poison``."""
+
+    def __init__(self, run, planner: AgentPlanner, *, poison: bool = True, gen_device="cuda",
+                 prefix_pass: Optional[str] = None):
+        self.run, self.plan = run, planner
+        dev = torch.device("cuda")
+        shape = (planner.num_blocks, run.num_kv_heads, BLOCK_SIZE, run.head_dim)
+        fill = float("nan") if poison else 0.0
+        self.kp = torch.full(shape, fill, dtype=run.dtype, device=dev)
+        self.vp = torch.full(shape, fill, dtype=run.dtype, device=dev)
+        S = run.num_seqs
+        self.rows = [run.seq_kv(s, gen_device) for s in range(S)]
+        # prefill rows through pkv_append
+        ks, vs, sl = [], [], []
+        for s, lo, hi, slots in planner.prefill():
+            k, v = self.rows[s]
+            ks.append(k[lo:hi].to(dev))
+            vs.append(v[lo:hi].to(dev))
+            sl.append(slots)
+        pkv_append(torch.cat(ks), torch.cat(vs), self.kp, self.vp,
+                   torch.from_numpy(np.concatenate(sl).astype(np.int64)).to(dev))
+        # the step's rows and queries, resident on the device
+        self.step_k, self.step_v, self.step_q = [], [], []
+        for i in range(run.steps):
+            pos = [p + i for p in run.prompt]
+            self.step_k.append(torch.stack([self.rows[s][0][pos[s]] for s in range(S)]).to(dev))
+            self.step_v.append(torch.stack([self.rows[s][1][pos[s]] for s in range(S)]).to(dev))
+            self.step_q.append(run.step_q(i, gen_device).to(dev))
+        self.qsl = torch.arange(S + 1, dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.step_q[0])
+        self.prefix_pass = prefix_pass
+        if prefix_pass is not None:
+            self.group = torch.zeros(S, dtype=torch.int32, device=dev)
+            self.plen = torch.tensor([run.shared_prefix], dtype=torch.int32, device=dev)
+            need = pkv_attention_shared_prefix_workspace_size(
+                S, S, 1, run.max_seqlen_k, run.num_q_heads, run.num_kv_heads, run.head_dim,
+                BLOCK_SIZE, run.dtype, num_groups=1, max_group_size=S,
+                max_prefix_len=run.shared_prefix)
+        else:
+            need = pkv_attention_workspace_size(S, S, 1, run.max_seqlen_k, run.num_q_heads,
+                                                run.num_kv_heads, run.head_dim, BLOCK_SIZE,
+                                                run.dtype)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        # step metadata: pinned host staging, two sets used in turn (a set is
+        # refilled only after the copy that read it two steps ago completed)
+        W = planner.width
+        self._h = [dict(slots=torch.empty(S, dtype=torch.int64).pin_memory(),
+                        table=torch.empty((S, W), dtype=torch.int32).pin_memory(),
+                        lens=torch.empty(S, dtype=torch.int32).pin_memory(),
+                        cow=torch.empty((2, S), dtype=torch.int32).pin_memory()) for _ in range(2)]
+        self._d = [{k: torch.empty_like(v, device=dev) for k, v in h.items()} for h in self._h]
+        self._ev = [None, None]
+        torch.cuda.synchronize()
+
+    def step(self, i: int, ev=None) -> torch.Tensor:
+        """Runs decode step i (host planning, upload, copies, append,
+        attention) and returns ``out`` [S, Hq, D] (overwritten by the next
+        step).  ``ev``: optional (start, end) CUDA events around attention."""
+        run = self.run
+        plan = self.plan.step(i)
+        b = i % 2
+        if self._ev[b] is not None:
+            self._ev[b].synchronize()
+        h, d = self._h[b], self._d[b]
+        h["slots"].numpy()[:] = plan.slots
+        h["table"].numpy()[:] = plan.table
+        h["lens"].numpy()[:] = plan.lens
+        d["slots"].copy_(h["slots"], non_blocking=True)
+        d["table"].copy_(h["table"], non_blocking=True)
+        d["lens"].copy_(h["lens"], non_blocking=True)
+        if plan.copies:
+            n = len(plan.copies)
+            h["cow"].numpy()[:, :n] = np.array(plan.copies, dtype=np.int32).T
+            d["cow"].copy_(h["cow"], non_blocking=True)
+            pkv_copy_blocks(self.kp, self.vp, d["cow"][0, :n], d["cow"][1, :n])
+        e = torch.cuda.Event()
+        e.record()
+        self._ev[b] = e
+        pkv_append(self.step_k[i], self.step_v[i], self.kp, self.vp, d["slots"])
+        if ev is not None:
+            ev[0].record()
+        if self.prefix_pass is not None:
+            pkv_attention_shared_prefix(
+                self.step_q[i], self.kp, self.vp, d["table"], d["lens"], self.qsl, run.scale,
+                self.group, self.plen, max_group_size=run.num_seqs,
+                max_prefix_len=run.shared_prefix, max_seqlen_q=1, max_seqlen_k=run.max_seqlen_k,
+                out=self.out, workspace=self.ws, prefix_pass=self.prefix_pass)
+        else:
+            pkv_attention(self.step_q[i], self.kp, self.vp, d["table"], d["lens"], self.qsl,
+                          run.scale, max_seqlen_q=1, max_seqlen_k=run.max_seqlen_k, out=self.out,
+                          workspace=self.ws)
+        if ev is not None:
+            ev[1].record()
+        return self.out

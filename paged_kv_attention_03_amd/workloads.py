@@ -321,113 +321,65 @@ def agent_lengths(seed: int = 4000, n: int = 16) -> List[int]:
 
 
 class AgentRun:
-    """Config 4: 16 sequences that share a 512-token prefix held in common
-    physical pages, each growing by one decode token per step for 70 steps.
-    Each step appends one row per sequence (taking a fresh page from a
-    shuffled free list when the sequence crosses a page boundary) and then
-    runs attention."""
+    """Config 4's inputs: 16 sequences whose prompts share a 512-token prefix,
+    each growing by one decode token per step for 70 steps (40 q / 8 kv heads,
+    head_dim 128, bf16).  Rows, lengths and queries only: which pages hold
+    the rows is decided by whoever lays out the pool (the host pool manager in
+    the engine loop, or a test's own layout)."""
 
-    def __init__(self, *, device="cpu", steps: int = 70, dtype=None, poison: bool = True,
-                 num_q_heads: int = 40, num_kv_heads: int = 8, head_dim: int = 128,
+    def __init__(self, *, steps: int = 70, dtype=None, num_q_heads: int = 40,
+                 num_kv_heads: int = 8, head_dim: int = 128,
                  prompt_lens: Optional[Sequence[int]] = None, shared_prefix: int = 512,
-                 duplicate_prefix: bool = False, seed: int = 4000):
-        dt = dtype or torch.bfloat16
+                 seed: int = 4000):
+        if shared_prefix % BLOCK_SIZE:
+            raise ValueError("the shared prefix must fill whole pages")
+        self.name = CONFIG_NAMES[4]
         self.steps = steps
+        self.dtype = dtype or torch.bfloat16
+        self.num_q_heads = num_q_heads
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
         self.prompt = list(prompt_lens) if prompt_lens is not None else agent_lengths(seed)
-        final = [p + steps for p in self.prompt]
-        bs = BLOCK_SIZE
-        S = len(self.prompt)
-        need = sum((f + bs - 1) // bs for f in final)
-        if not duplicate_prefix:
-            need -= (S - 1) * (shared_prefix // bs)
-        num_blocks = int(math.ceil(1.25 * need))
-        # Every page is drawn up front from the shuffled pool; a page that a
-        # sequence reaches only during the loop enters its block-table row when
-        # the sequence crosses into it (see :meth:`step`), and until then the
-        # row holds -1 there.
-        base = build_step(CONFIG_NAMES[4], final, [1] * S, num_q_heads, num_kv_heads, head_dim,
-                          dt, seed, device=device, num_blocks=num_blocks,
-                          shared_prefix=0 if duplicate_prefix else shared_prefix,
-                          poison=poison)
-        if duplicate_prefix:
-            base.shared_prefix = 0
-            self._dup_prefix = shared_prefix
-        else:
-            self._dup_prefix = 0
-        self.base = base
+        if min(self.prompt) < shared_prefix:
+            raise ValueError("every prompt must hold the shared prefix")
+        self.shared_prefix = shared_prefix
         self.seed = seed
-        # pages each sequence holds before the loop; later pages come from a
-        # free list in the order sequences cross page boundaries
-        self._bt_full = base.block_tables.copy()
-        self.block_tables = np.full_like(self._bt_full, -1)
-        for s in range(S):
-            npg = (self.prompt[s] + bs - 1) // bs
-            self.block_tables[s, :npg] = self._bt_full[s, :npg]
-        if duplicate_prefix:
-            # same rows as the shared run, prefix stored per sequence
-            self.base.seq_kv = self._dup_seq_kv  # type: ignore[assignment]
-
-    def _dup_seq_kv(self, s, device=None):
-        b = self.base
-        dev = device or b.device
-        n = b.real_lens[s]
-        shp = (b.num_kv_heads, b.head_dim)
-        P = self._dup_prefix
-        k = [randn((P,) + shp, self.seed + 3, dev, b.dtype)[:min(P, n)]]
-        v = [randn((P,) + shp, self.seed + 4, dev, b.dtype)[:min(P, n)]]
-        if n > P:
-            k.append(randn((n - P,) + shp, self.seed + 10000 + s, dev, b.dtype))
-            v.append(randn((n - P,) + shp, self.seed + 20000 + s, dev, b.dtype))
-        return torch.cat(k, 0), torch.cat(v, 0)
+        self.scale = float(np.float32(1.0 / math.sqrt(head_dim)))
 
     @property
-    def shared_pages(self) -> List[int]:
-        return self.base.shared_pages
+    def num_seqs(self) -> int:
+        return len(self.prompt)
 
-    def prefill_rows(self, device=None):
-        """Rows of every prompt (the state before the first decode step)."""
-        b = self.base
-        dev = device or b.device
-        ks, vs, sl = [], [], []
-        wrote = False
-        for s in range(b.num_seqs):
-            k, v = b.seq_kv(s, dev)
-            lo = 0
-            if b.shared_prefix > 0 and wrote:
-                lo = b.shared_prefix
-            wrote = True
-            ks.append(k[lo:self.prompt[s]])
-            vs.append(v[lo:self.prompt[s]])
-            sl.append(b.token_slots[s][lo:self.prompt[s]])
-        return (torch.cat(ks, 0), torch.cat(vs, 0),
-                torch.from_numpy(np.concatenate(sl).astype(np.int64)).to(dev))
+    @property
+    def final_lens(self) -> List[int]:
+        return [p + self.steps for p in self.prompt]
 
-    def step(self, i: int):
-        """Host metadata of decode step i (0-based): the new rows to append,
-        their slots, the block tables after any page allocation, seq_lens."""
-        b = self.base
-        bs = b.block_size
-        pos = [p + i for p in self.prompt]        # position of the new token
-        for s in range(b.num_seqs):
-            npg = pos[s] // bs + 1                # a page crossing adds one entry
-            self.block_tables[s, :npg] = self._bt_full[s, :npg]
-        slots = np.array([b.token_slots[s][pos[s]] for s in range(b.num_seqs)], dtype=np.int64)
-        seq_lens = [p + 1 for p in pos]
-        return pos, slots, self.block_tables.copy(), seq_lens
+    @property
+    def max_seqlen_k(self) -> int:
+        return max(self.final_lens)
 
-    def step_rows(self, i: int, device=None):
-        b = self.base
-        dev = device or b.device
-        pos = [p + i for p in self.prompt]
-        ks, vs = [], []
-        for s in range(b.num_seqs):
-            k, v = b.seq_kv(s, dev)
-            ks.append(k[pos[s]:pos[s] + 1])
-            vs.append(v[pos[s]:pos[s] + 1])
-        return torch.cat(ks, 0), torch.cat(vs, 0)
+    def seq_lens_at(self, i: int) -> List[int]:
+        """Keys of every sequence in decode step i (0-based), its new token included."""
+        return [p + i + 1 for p in self.prompt]
 
-    def step_q(self, i: int, device=None):
-        b = self.base
-        dev = device or b.device
-        return randn((b.num_seqs, b.num_q_heads, b.head_dim), self.seed + 1 + 7919 * (i + 1), dev,
-                     b.dtype)
+    def seq_kv(self, s: int, device="cpu"):
+        """All rows sequence s will hold, [prompt + steps, Hkv, D] each: the
+        shared prefix rows first (the same for every sequence), then its own."""
+        shp = (self.num_kv_heads, self.head_dim)
+        P = self.shared_prefix
+        n = self.prompt[s] + self.steps
+        k = [randn((P,) + shp, self.seed + 3, device, self.dtype)] if P else []
+        v = [randn((P,) + shp, self.seed + 4, device, self.dtype)] if P else []
+        k.append(randn((n - P,) + shp, self.seed + 10000 + s, device, self.dtype))
+        v.append(randn((n - P,) + shp, self.seed + 20000 + s, device, self.dtype))
+        return torch.cat(k, 0), torch.cat(v, 0)
+
+    def step_q(self, i: int, device="cpu"):
+        return randn((self.num_seqs, self.num_q_heads, self.head_dim),
+                     self.seed + 1 + 7919 * (i + 1), device, self.dtype)
+
+    def free_order(self, num_blocks: int) -> np.ndarray:
+        """The order in which a pool of num_blocks pages hands out its free
+        pages: a seeded shuffle (a pool that has served for a while hands out
+        pages in no particular order)."""
+        return np.random.default_rng(self.seed + 17).permutation(num_blocks).astype(np.int32)

@@ -7,7 +7,7 @@
 // checks that invalid calls fail with their documented codes and launch
 // nothing.  Exit status 0 when every check passes.
 //
-// Built by __graft_entry__.build(); run by tests/test_gpu_c_client.py.
+// Built by __graft_entry__.build(); run by tests/test_c_client.py.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -178,8 +178,11 @@ int run_case(pkv_dtype_t dtype) {
 
     check(pkv_check_slots(slots.data(), T, BS, num_blocks) == PKV_OK, "pkv_check_slots");
     check(pkv_check_metadata(bt.data(), lens.data(), qsl.data(), nullptr, S, total_q, max_blocks,
-                             BS, num_blocks) == PKV_OK,
+                             max_q, max_k, BS, num_blocks) == PKV_OK,
           "pkv_check_metadata");
+    check(pkv_check_metadata(bt.data(), lens.data(), qsl.data(), nullptr, S, total_q, max_blocks,
+                             max_q - 1, max_k, BS, num_blocks) == PKV_E_METADATA,
+          "pkv_check_metadata rejects an understated max_seqlen_q");
     int rc = pkv_append(d_knew, d_vnew, d_kpool, d_vpool, (const int64_t*)d_slots, T, Hkv, D, BS,
                         num_blocks, dtype, stream);
     check(rc == PKV_OK, "pkv_append");

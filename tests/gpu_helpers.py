@@ -69,17 +69,62 @@ def oracle_seq_outputs(st, q_host, seqs, gen_device="cpu", tokens=None):
     return res
 
 
+def contiguous_pool(rows, num_kv_heads, head_dim, dtype, bs=16):
+    """Oracle-side layout of whole sequences: sequence i's rows ``rows[i] =
+    (k, v)`` fill pages base_i, base_i + 1, ... of a pool written by the
+    oracle's append (unwritten bytes NaN); returns (k_pool, v_pool, block
+    tables) with -1 past each sequence's pages.  Built from the generator's
+    rows alone."""
+    npg = [max(1, (k.shape[0] + bs - 1) // bs) for k, _ in rows]
+    base = np.concatenate([[0], np.cumsum(npg)]).astype(np.int64)
+    shape = (int(base[-1]), num_kv_heads, bs, head_dim)
+    kp = torch.full(shape, float("nan"), dtype=dtype)
+    vp = kp.clone()
+    ks = torch.cat([k for k, _ in rows])
+    vs = torch.cat([v for _, v in rows])
+    slots = np.concatenate([base[i] * bs + np.arange(k.shape[0], dtype=np.int64)
+                            for i, (k, _) in enumerate(rows)])
+    kp, vp = oracle.oracle_append(kp, vp, ks, vs, slots)
+    bt = np.full((len(rows), max(npg)), -1, dtype=np.int32)
+    for i, n in enumerate(npg):
+        bt[i, :n] = np.arange(base[i], base[i] + n, dtype=np.int32)
+    return kp, vp, bt
+
+
+def oracle_batches(st, q_host, gen_device="cpu", batch=16):
+    """Oracle outputs of every sequence of a step, ``batch`` sequences per
+    oracle call, each from its real rows (drawn on ``gen_device``) in a
+    contiguous pool: yields (first query row, last query row + 1, float64
+    [rows, Hq, D])."""
+    qsl = st.query_start_loc()
+    for s0 in range(0, st.num_seqs, batch):
+        seqs = list(range(s0, min(s0 + batch, st.num_seqs)))
+        rows = []
+        for s in seqs:
+            k, v = st.seq_kv(s, gen_device)
+            rows.append((k.cpu(), v.cpu()))
+        kp, vp, bt = contiguous_pool(rows, st.num_kv_heads, st.head_dim, st.dtype)
+        lens = [k.shape[0] for k, _ in rows]
+        q0, q1 = int(qsl[seqs[0]]), int(qsl[seqs[-1] + 1])
+        sub_qsl = (qsl[seqs[0]:seqs[-1] + 2] - q0).astype(np.int32)
+        ref = oracle.oracle_attention(q_host[q0:q1], kp, vp, bt, lens, sub_qsl, st.scale)
+        del kp, vp, rows
+        yield q0, q1, ref
+
+
 def to_f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def check_close(got, ref, dtype, what):
+def check_close(got, ref, dtype, what, quiet=False):
     atol, rtol = TOL[dtype]
     g = to_f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     ok, maxerr = close(g, ref, atol, rtol)
     denom = float(np.linalg.norm(ref)) or 1.0
     rel = float(np.linalg.norm(np.nan_to_num(g - ref, nan=1e30))) / denom
-    log(f"  {what}: max|err| {maxerr:.3e}  rel-L2 {rel:.3e}  finite {bool(np.isfinite(g).all())}")
+    if not quiet or not ok:
+        log(f"  {what}: max|err| {maxerr:.3e}  rel-L2 {rel:.3e}  "
+            f"finite {bool(np.isfinite(g).all())}")
     assert ok, f"{what}: outside atol={atol} rtol={rtol} (max err {maxerr:.3e})"
     return maxerr, rel
 

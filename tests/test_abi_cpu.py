@@ -133,11 +133,31 @@ def test_checker_accepts_every_config(k):
 
 
 def test_checker_accepts_agent_run_steps():
+    # the host side of the agent loop (pool manager, no GPU): every step's
+    # metadata passes the checkers, the new token's slot is the next key of
+    # its sequence, and the shared prefix pages are never a write target
+    from paged_kv_attention_03_amd.engine import AgentPlanner
     run = W.AgentRun(steps=70)
-    for i in (0, 35, 69):
-        pos, slots, bt, sl = run.step(i)
-        pkv.pkv_check_metadata(bt, sl, np.arange(17), None, 16, 16, run.base.num_blocks)
-        pkv.pkv_check_slots(slots, 16, run.base.num_blocks)
+    planner = AgentPlanner(run)
+    segs = planner.prefill()
+    slots = np.concatenate([sl for _, _, _, sl in segs])
+    pkv.pkv_check_slots(slots, 16, planner.num_blocks)
+    assert sum(hi - lo for _, lo, hi, _ in segs) == sum(run.prompt) - 15 * run.shared_prefix
+    shared = set(planner.shared_pages)
+    assert len(shared) == run.shared_prefix // 16
+    for i in range(run.steps):
+        plan = planner.step(i)
+        assert not plan.copies
+        assert list(plan.lens) == run.seq_lens_at(i)
+        pkv.pkv_check_metadata(plan.table, plan.lens, np.arange(17), None, 16, 16,
+                               planner.num_blocks, max_seqlen_q=1, max_seqlen_k=run.max_seqlen_k)
+        pkv.pkv_check_slots(plan.slots, 16, planner.num_blocks)
+        pos = plan.lens - 1
+        assert (plan.table[np.arange(16), pos // 16].astype(np.int64) * 16 + pos % 16
+                == plan.slots).all()
+        assert not set((plan.slots // 16).tolist()) & shared
+        assert all(set(plan.table[s, :32].tolist()) == shared for s in range(16))
+    planner.close()
 
 
 def _meta():
@@ -164,6 +184,25 @@ def test_checker_rejects_bad_metadata(mutate):
     assert e.value.code == pkv.PKV_E_METADATA
 
 
+def test_checker_enforces_the_host_bounds():
+    # understated bounds would leave output rows unwritten (max_seqlen_q) or
+    # drop keys (max_seqlen_k) without an error from pkv_attention
+    st = W.config_step(3)
+    md = st.metadata("cpu")
+    args = (md["block_tables"], md["seq_lens"], md["query_start_loc"], None, st.total_q,
+            st.block_size, st.num_blocks)
+    pkv.pkv_check_metadata(*args, max_seqlen_q=st.max_seqlen_q, max_seqlen_k=st.max_seqlen_k)
+    pkv.pkv_check_metadata(*args)  # the step's own maxima
+    for kw in (dict(max_seqlen_q=1, max_seqlen_k=st.max_seqlen_k),
+               dict(max_seqlen_q=st.max_seqlen_q - 1, max_seqlen_k=st.max_seqlen_k),
+               dict(max_seqlen_q=st.max_seqlen_q, max_seqlen_k=st.max_seqlen_k - 1)):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_check_metadata(*args, **kw)
+        assert e.value.code == pkv.PKV_E_METADATA
+    lib = pkv.load_library()
+    assert lib.pkv_check_metadata(None, None, None, None, 1, 1, 1, -1, 1, 16, 1) == pkv.PKV_E_ARG
+
+
 def test_checker_rejects_bad_slots():
     with pytest.raises(pkv.PkvError):
         pkv.pkv_check_slots([0, 5, 5], 16, 4)
@@ -185,13 +224,14 @@ def _sp(lib, **over):
     a = dict(out=FAKE, q=FAKE + 0x10000000, k=FAKE + 0x20000000, v=FAKE + 0x30000000, bt=FAKE,
              sl=FAKE, qsl=FAKE, pg=FAKE, pl=FAKE, ng=1, mgs=4, mpl=64, num_seqs=4, total_q=4,
              max_blocks=8, msq=1, msk=100, hq=8, hkv=2, d=128, bs=16, nb=64, scale=0.125,
-             dtype=pkv.PKV_BF16, ws=None, ws_bytes=0, stream=None)
+             dtype=pkv.PKV_BF16, route=pkv.PKV_PREFIX_PASS_ALWAYS, ws=None, ws_bytes=0,
+             stream=None)
     a.update(over)
     return lib.pkv_attention_shared_prefix(
         a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["qsl"], a["pg"], a["pl"], a["ng"],
         a["mgs"], a["mpl"], a["num_seqs"], a["total_q"], a["max_blocks"], a["msq"], a["msk"],
-        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"], a["ws"],
-        a["ws_bytes"], a["stream"])
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"], a["route"],
+        a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("over,code", [
@@ -205,7 +245,13 @@ def _sp(lib, **over):
     (dict(mpl=112), pkv.PKV_E_ARG),            # not below max_seqlen_k
     (dict(d=96), pkv.PKV_E_UNSUPPORTED),       # checked as for pkv_attention
     (dict(scale=0.0), pkv.PKV_E_ARG),
+    (dict(bs=0), pkv.PKV_E_UNSUPPORTED),        # checked before the prefix length is
+    (dict(bs=-1), pkv.PKV_E_UNSUPPORTED),       # divided by it (no division by zero)
+    (dict(bs=0, mpl=0), pkv.PKV_E_UNSUPPORTED),
+    (dict(route=2), pkv.PKV_E_ARG),
+    (dict(route=-1), pkv.PKV_E_ARG),
     (dict(), pkv.PKV_E_WORKSPACE),
+    (dict(route=pkv.PKV_PREFIX_PASS_AUTO), pkv.PKV_E_WORKSPACE),  # sized for the pass either way
 ])
 def test_shared_prefix_rejects_invalid_arguments(lib, over, code):
     assert _sp(lib, **over) == code

@@ -129,29 +129,22 @@ def test_runs_are_bitwise_deterministic():
 
 @pytest.mark.gpu
 def test_shared_prefix_equals_duplicated_prefix_bitwise():
-    common = dict(steps=5, num_q_heads=16, num_kv_heads=2, head_dim=128,
-                  prompt_lens=[600, 517, 1000, 530], shared_prefix=512)
-    runs = [W.AgentRun(**common), W.AgentRun(duplicate_prefix=True, **common)]
-    pools = []
-    for run in runs:
-        kp, vp = run.base.new_pool("cuda")
-        k, v, s = run.prefill_rows("cpu")
-        pkv.pkv_append(k.cuda(), v.cuda(), kp, vp, s.cuda())
-        pools.append((kp, vp))
-    for i in range(5):
-        outs = []
-        for run, (kp, vp) in zip(runs, pools):
-            pos, slots, bt, sl = run.step(i)
-            k, v = run.step_rows(i, "cpu")
-            pkv.pkv_append(k.cuda(), v.cuda(), kp, vp, torch.from_numpy(slots).cuda())
-            q = run.step_q(i, "cpu").cuda()
-            out = pkv.pkv_attention(q, kp, vp, torch.from_numpy(bt).cuda(),
-                                    torch.tensor(sl, dtype=torch.int32, device="cuda"),
-                                    torch.arange(5, dtype=torch.int32, device="cuda"),
-                                    run.base.scale, max_seqlen_q=1, max_seqlen_k=max(sl))
-            torch.cuda.synchronize()
-            outs.append(raw_bits(out))
+    # the pool manager forks the prefix (pages held in common) in one loop and
+    # gives every sequence its own copy in the other
+    from paged_kv_attention_03_amd.engine import AgentLoop, AgentPlanner
+    run = W.AgentRun(steps=5, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                     prompt_lens=[600, 517, 1000, 530], shared_prefix=512)
+    loops = []
+    for share in (True, False):
+        planner = AgentPlanner(run, share_prefix=share)
+        loops.append(AgentLoop(run, planner, poison=True, gen_device="cpu"))
+    assert len(loops[0].plan.shared_pages) == 32 and not loops[1].plan.shared_pages
+    for i in range(run.steps):
+        outs = [raw_bits(lp.step(i)).copy() for lp in loops]
+        torch.cuda.synchronize()
         assert np.array_equal(outs[0], outs[1]), f"step {i}"
+    for lp in loops:
+        lp.plan.close()
 
 
 @pytest.mark.gpu

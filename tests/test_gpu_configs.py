@@ -4,9 +4,9 @@
 4 the 70-step agent loop over a shared 512-token prefix, 5 the 128-sequence
 large decode (ragged and left-padded to a common offset).  The bf16 runs use
 atol = rtol = 1e-2; float32 "shadow" runs of the same shapes use 1e-5, which a
-single leaked or dropped key would break.  Configs 1-4 are checked on every
-output; config 5 on sampled sequences (all heads), the longest and shortest
-among them, plus the left-padded run against the ragged one everywhere."""
+single leaked or dropped key would break.  Every output of every config is
+compared with the oracle: config 4 at each of its 70 steps, config 5 on all
+128 sequences of both the ragged and the left-padded run."""
 import numpy as np
 import pytest
 import torch
@@ -14,8 +14,9 @@ import torch
 import oracle
 import paged_kv_attention_03_amd as pkv
 from paged_kv_attention_03_amd import workloads as W
-from tests.gpu_helpers import (TOL, check_close, gpu_attention, gpu_pools, log, oracle_seq_outputs,
-                               raw_bits)
+from paged_kv_attention_03_amd.engine import AgentLoop, AgentPlanner
+from tests.gpu_helpers import (TOL, check_close, contiguous_pool, gpu_attention, gpu_pools, log,
+                               oracle_batches, raw_bits)
 from tests.helpers import close, oracle_pools, oracle_step
 
 
@@ -47,49 +48,56 @@ def test_config_full(k, dtype):
 @pytest.mark.gpu
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32-shadow"])
 def test_config4_agent_loop(dtype):
+    """The 70-step agent loop as an engine runs it: the host pool manager forks
+    the 512-token prefix (its pages held in common), hands out one slot per
+    sequence each step from a shuffled free list and exports the block tables;
+    each step appends, then attends.  Every step's output is compared with the
+    oracle, which computes each sequence from the generator's rows in its own
+    contiguous layout (nothing of the manager's)."""
     run = W.AgentRun(dtype=dtype)
-    b = run.base
-    log(f"config 4 agent loop dtype={dtype} prompts={run.prompt} pages={b.num_blocks}")
-    kp, vp = b.new_pool("cuda")
-    k, v, s = run.prefill_rows("cpu")
-    pkv.pkv_append(k.cuda(), v.cuda(), kp, vp, s.cuda())
-    okp, ovp = oracle.oracle_append(*b.new_pool("cpu"), k, v, s)
-    shared = torch.tensor(run.shared_pages, device="cuda")
-    shared_before = (raw_bits(kp[shared]).copy(), raw_bits(vp[shared]).copy())
-    qsl = torch.arange(b.num_seqs + 1, dtype=torch.int32, device="cuda")
-    check_steps = {0, 1, 2, 17, 34, 51, 68, 69} if dtype == torch.bfloat16 else {0, 33, 69}
-    ws = None
+    planner = AgentPlanner(run)
+    loop = AgentLoop(run, planner, poison=True, gen_device="cpu")
+    S = run.num_seqs
+    log(f"config 4 agent loop dtype={dtype} prompts={run.prompt} pages={planner.num_blocks} "
+        f"shared pages={planner.shared_pages}")
+    okp, ovp, obt = contiguous_pool([(k.cpu(), v.cpu()) for k, v in loop.rows], run.num_kv_heads,
+                                    run.head_dim, dtype)
+    shared = torch.tensor(planner.shared_pages, device="cuda")
+    assert len(planner.shared_pages) == run.shared_prefix // 16
+    shared_before = (raw_bits(loop.kp[shared]).copy(), raw_bits(loop.vp[shared]).copy())
+    qsl = np.arange(S + 1, dtype=np.int32)
+    worst = 0.0
     for i in range(run.steps):
-        pos, slots, bt, sl = run.step(i)
-        assert not set(slots // 16) & set(run.shared_pages)
-        kn, vn = run.step_rows(i, "cpu")
-        pkv.pkv_append(kn.cuda(), vn.cuda(), kp, vp, torch.from_numpy(slots).cuda())
-        okp, ovp = oracle.oracle_append(okp, ovp, kn, vn, slots)
-        q = run.step_q(i, "cpu")
-        if ws is None:
-            need = pkv.pkv_attention_workspace_size(b.num_seqs, b.num_seqs, 1, max(run.prompt) + 70,
-                                                    b.num_q_heads, b.num_kv_heads, b.head_dim,
-                                                    16, dtype)
-            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-        out = pkv.pkv_attention(q.cuda(), kp, vp, torch.from_numpy(bt).cuda(),
-                                torch.tensor(sl, dtype=torch.int32, device="cuda"), qsl, b.scale,
-                                max_seqlen_q=1, max_seqlen_k=max(run.prompt) + 70, workspace=ws)
-        if i in check_steps:
-            torch.cuda.synchronize()
-            ref = oracle.oracle_attention(q, okp, ovp, bt, sl, np.arange(b.num_seqs + 1), b.scale)
-            check_close(out, ref, dtype, f"step {i}")
-    torch.cuda.synchronize()
-    assert np.array_equal(raw_bits(kp), okp.view(raw_bits(kp).dtype)), "pool bytes after 70 steps"
-    assert np.array_equal(raw_bits(vp), ovp.view(raw_bits(vp).dtype))
-    assert np.array_equal(raw_bits(kp[shared]), shared_before[0]), "shared prefix pages changed"
-    assert np.array_equal(raw_bits(vp[shared]), shared_before[1])
-    del kp, vp
+        out = loop.step(i)
+        torch.cuda.synchronize()
+        ref = oracle.oracle_attention(run.step_q(i, "cpu"), okp, ovp, obt, run.seq_lens_at(i), qsl,
+                                      run.scale)
+        err, _ = check_close(out, ref, dtype, f"step {i}", quiet=i not in (0, 69))
+        worst = max(worst, err)
+    log(f"  all {run.steps} steps within tolerance (max |err| {worst:.3e})")
+    # the pool read back through the manager's block tables holds every
+    # sequence's rows, byte for byte; the shared prefix pages never changed
+    table, lens = planner.pool.block_tables(list(range(S)), planner.width)
+    assert list(lens) == run.final_lens
+    for s in range(S):
+        n = run.final_lens[s]
+        pages = torch.from_numpy(table[s][:(n + 15) // 16].astype(np.int64)).cuda()
+        for pool, want in ((loop.kp, loop.rows[s][0]), (loop.vp, loop.rows[s][1])):
+            got = pool[pages].permute(0, 2, 1, 3).reshape(-1, run.num_kv_heads, run.head_dim)[:n]
+            assert np.array_equal(raw_bits(got), raw_bits(want)), f"sequence {s} rows"
+    assert np.array_equal(raw_bits(loop.kp[shared]), shared_before[0]), "shared prefix pages changed"
+    assert np.array_equal(raw_bits(loop.vp[shared]), shared_before[1])
+    planner.close()
+    del loop
     _free()
 
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32-shadow"])
 def test_config5_large_decode_ragged_and_padded(dtype):
+    """All 128 sequences, every head, of both the ragged and the left-padded
+    run against the oracle (16 sequences per oracle call, each from its real
+    rows in a contiguous layout), plus padded == ragged to the same tolerance."""
     rag = W.config_step(5, dtype=dtype)
     pad = W.config_step(5, dtype=dtype, padded=True)
     lens = rag.seq_lens
@@ -97,23 +105,24 @@ def test_config5_large_decode_ragged_and_padded(dtype):
         f"max={max(lens)} min={min(lens)}")
     q = rag.make_q("cuda")
     kp, vp = gpu_pools(rag, "cuda")
-    out_rag = gpu_attention(rag, q, kp, vp)
+    out_rag = gpu_attention(rag, q, kp, vp).cpu()
     log("  ragged step done")
     del kp, vp
     _free()
     kp, vp = gpu_pools(pad, "cuda")
-    out_pad = gpu_attention(pad, q, kp, vp)
+    out_pad = gpu_attention(pad, q, kp, vp).cpu()
     log(f"  padded step done (kv_start up to {max(pad.kv_start)})")
     del kp, vp
     _free()
-    sample = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 0, 77})
-    ref = oracle_seq_outputs(rag, q.cpu(), sample, "cuda")
-    for s in sample:
-        check_close(out_rag[s:s + 1], ref[s], dtype, f"ragged seq {s} (L={lens[s]})")
-        check_close(out_pad[s:s + 1], ref[s], dtype, f"padded seq {s}")
-    # padded == ragged on every output, to the same tolerance
+    q_host = q.cpu()
+    worst = {"ragged": 0.0, "padded": 0.0}
+    for q0, q1, ref in oracle_batches(rag, q_host, "cuda"):
+        for name, out in (("ragged", out_rag), ("padded", out_pad)):
+            err, _ = check_close(out[q0:q1], ref, dtype, f"{name} seqs {q0}..{q1 - 1}", quiet=True)
+            worst[name] = max(worst[name], err)
+    log(f"  all 128 sequences vs oracle: max |err| ragged {worst['ragged']:.3e}, "
+        f"padded {worst['padded']:.3e}")
     atol, rtol = TOL[dtype]
-    ok, err = close(out_pad.float().cpu().numpy(), out_rag.float().cpu().numpy().astype(np.float64),
-                    atol, rtol)
+    ok, err = close(out_pad.float().numpy(), out_rag.float().numpy().astype(np.float64), atol, rtol)
     log(f"  padded vs ragged, all 128 sequences: max|diff| {err:.3e}")
     assert ok

@@ -96,7 +96,8 @@ def test_shared_prefix_step_replays_from_a_graph(monkeypatch):
     def call(out):
         pkv.pkv_attention_shared_prefix(q, kp, vp, bt, lens, qsl, st["scale"], grp, plen,
                                         max_group_size=16, max_prefix_len=512, max_seqlen_q=mq,
-                                        max_seqlen_k=mk, out=out, workspace=ws)
+                                        max_seqlen_k=mk, out=out, workspace=ws,
+                                        prefix_pass="always")
 
     eager = torch.empty_like(q)
     call(eager)

@@ -76,7 +76,7 @@ def build(groups, plain, hq, hkv, D, dtype, seed):
                 scale=float(np.float32(1.0 / math.sqrt(D))))
 
 
-def run_both(st, max_group_size, max_prefix_len, repeat=1):
+def run_both(st, max_group_size, max_prefix_len, repeat=1, prefix_pass="always"):
     dev = "cuda"
     q = st["q"].to(dev)
     kp, vp = st["kp"].to(dev), st["vp"].to(dev)
@@ -90,7 +90,8 @@ def run_both(st, max_group_size, max_prefix_len, repeat=1):
     for _ in range(repeat):
         outs.append(pkv.pkv_attention_shared_prefix(
             q, kp, vp, bt, lens, qsl, st["scale"], grp, plen, max_group_size=max_group_size,
-            max_prefix_len=max_prefix_len, max_seqlen_q=mq, max_seqlen_k=mk))
+            max_prefix_len=max_prefix_len, max_seqlen_q=mq, max_seqlen_k=mk,
+            prefix_pass=prefix_pass))
     plain = pkv.pkv_attention(q, kp, vp, bt, lens, qsl, st["scale"], max_seqlen_q=mq,
                               max_seqlen_k=mk)
     torch.cuda.synchronize()
@@ -157,3 +158,20 @@ def test_no_groups_is_plain_attention_bitwise():
     outs, plain, ref = run_both(st, 2, 64)
     assert np.array_equal(raw_bits(outs[0]), raw_bits(plain))
     check_close(outs[0], ref, torch.bfloat16, "no members")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("prefix,members,expect_pass", [(512, 16, False), (8192, 16, True)],
+                         ids=["agent-512x16-plain", "long-8192x16-pass"])
+def test_auto_routing_picks_a_path_bitwise(prefix, members, expect_pass):
+    # "auto" runs the prefix pass only when the re-reads it avoids reach
+    # 256 MiB: 15 x 512 keys x 4 KiB = 31 MB -> the plain path, bitwise equal
+    # to pkv_attention; 15 x 8192 keys x 4 KiB = 503 MB -> the prefix pass,
+    # bitwise equal to prefix_pass="always"
+    st = build([(prefix, [prefix + 1 + 37 * i for i in range(members)])], [], 40, 8, 128,
+               torch.bfloat16, 4242 + prefix)
+    auto, plain, ref = run_both(st, members, prefix, prefix_pass="auto")
+    always, _, _ = run_both(st, members, prefix, prefix_pass="always")
+    check_close(auto[0], ref, torch.bfloat16, f"auto {prefix}x{members}")
+    same = raw_bits(always[0]) if expect_pass else raw_bits(plain)
+    assert np.array_equal(raw_bits(auto[0]), same)

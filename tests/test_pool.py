@@ -275,3 +275,29 @@ def test_batch_append_is_all_or_nothing():
     assert before[1][0].tolist() == after[1][0].tolist()
     slots, _ = pool.append_batch([2, 1], [3, 2])
     assert pool.seq_len(1) == 2 and pool.seq_len(2) == 3 and len(slots) == 5
+
+
+def test_free_order_sets_page_placement():
+    pool = pkv.PagePool(8, 4, 2, 8)
+    order = [5, 2, 7, 0, 1, 6, 3, 4]
+    pool.set_free_order(order)
+    pool.add_seq(0)
+    slots, _ = pool.append(0, 10)               # 3 pages: 5, 2, 7
+    table, lens = pool.block_tables([0], 4)
+    assert list(table[0]) == [5, 2, 7, -1] and lens[0] == 10
+    assert list(slots) == [5 * 4 + i for i in range(4)] + [2 * 4 + i for i in range(4)] + [28, 29]
+    # the rest keep the given order; a released page goes back on top
+    pool.truncate(0, 4)                          # releases 7, then 2
+    pool.add_seq(1)
+    pool.append(1, 12)
+    table, _ = pool.block_tables([1], 4)
+    assert list(table[0][:3]) == [2, 7, 0]
+    # the order must be a permutation of exactly the free pages (1, 6, 3, 4)
+    for bad in ([1, 6, 3], [1, 6, 3, 4, 4], [1, 6, 3, 3], [1, 6, 3, 5], [1, 6, 3, 9]):
+        with pytest.raises(pkv.PkvError):
+            pool.set_free_order(bad)
+    assert pool.free_blocks == 4
+    pool.set_free_order([3, 1, 6, 4])
+    pool.append(0, 4)                            # its second page
+    table, _ = pool.block_tables([0], 4)
+    assert list(table[0][:3]) == [5, 3, -1]
