@@ -152,6 +152,34 @@ int pkv_attention(void *out, const void *q, const void *k_pool, const void *v_po
                   size_t workspace_bytes, void *stream);
 
 /*
+ * pkv_attention_noalloc -- pkv_attention without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * The step's workspace is a static device array of the library's own, of
+ * PKV_NOALLOC_SCRATCH_BYTES (24 MiB); every GPU the library runs on holds its
+ * own copy until the process ends (its address is looked up on the first
+ * call on each device).  The call itself allocates nothing.  Every argument
+ * is as for pkv_attention; a step whose pkv_attention_workspace_size exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES returns PKV_E_WORKSPACE and launches nothing (a
+ * decode window of 16 / G tokens at head_dim 128 takes ~16.3 MiB plus 36
+ * bytes per (sequence, kv head)).  Nothing in the scratch needs to start at
+ * zero: each call writes what it reads.  All calls on one GPU share its
+ * scratch, so two calls that may overlap on one GPU (different streams
+ * without an ordering between them, or several host threads) race; calls on
+ * one stream are ordered and safe.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+
+int pkv_attention_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                          const int32_t *block_tables, const int32_t *seq_lens,
+                          const int32_t *query_start_loc, const int32_t *kv_start, int num_seqs,
+                          int64_t total_q, int max_blocks_per_seq, int max_seqlen_q,
+                          int max_seqlen_k, int num_q_heads, int num_kv_heads, int head_dim,
+                          int block_size, int64_t num_blocks, float scale, pkv_dtype_t dtype,
+                          void *stream);
+
+/*
  * pkv_attention_shared_prefix -- pkv_attention for a step in which groups of
  * decode sequences share their first keys through common pages, reading
  * each group's shared pages once per kv head instead of once per sequence.

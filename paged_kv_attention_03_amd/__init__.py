@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "PKV_F32", "PKV_BF16", "PkvError", "pkv_append", "pkv_attention",
-    "pkv_attention_workspace_size", "pkv_attention_shared_prefix",
+    "pkv_attention_workspace_size", "pkv_attention_noalloc", "pkv_attention_shared_prefix",
     "pkv_attention_shared_prefix_workspace_size", "pkv_check_shared_prefix",
     "pkv_check_metadata", "pkv_check_slots", "pkv_last_error",
     "pkv_copy_blocks", "PagePool", "library_path", "load_library",
@@ -77,6 +77,9 @@ def load_library():
     lib.pkv_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                   i32, i32, i32, i64, ctypes.c_float, i32, vp, sz, vp]
     lib.pkv_attention.restype = i32
+    lib.pkv_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                          i32, i32, i32, i32, i64, ctypes.c_float, i32, vp]
+    lib.pkv_attention_noalloc.restype = i32
     lib.pkv_attention_shared_prefix_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32,
                                                                i32, i32, i32, i32, i32]
     lib.pkv_attention_shared_prefix_workspace_size.restype = sz
@@ -237,6 +240,46 @@ def pkv_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _raise(lib.pkv_attention(*ptrs, ns, total_q, max_blocks, int(max_seqlen_q), int(max_seqlen_k),
                              hq, hkv, d, bs, nb, float(scale), dt, ws_ptr, ws_bytes,
                              _stream(q.device, stream)))
+    return out
+
+
+def pkv_attention_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                          block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                          query_start_loc: torch.Tensor, scale: float, *, max_seqlen_q: int,
+                          max_seqlen_k: int, out: torch.Tensor,
+                          kv_start: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pkv_attention whose workspace is the library's static device scratch
+    (``PKV_NOALLOC_SCRATCH_BYTES``): neither the call nor this binding
+    allocates; ``out`` is the caller's.  Calls that may overlap on one GPU
+    share the scratch and race."""
+    lib = load_library()
+    dt = _dtype_code(q.dtype)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [total_q, Hq, D] and pools [num_blocks, Hkv, bs, D]")
+    total_q, hq, d = q.shape
+    nb, hkv, bs, d2 = k_pool.shape
+    if d2 != d:
+        raise ValueError("head_dim of q and pools differ")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    ns, max_blocks = block_tables.shape
+    if seq_lens.shape != (ns,) or query_start_loc.shape != (ns + 1,):
+        raise ValueError("seq_lens must be [num_seqs] and query_start_loc [num_seqs + 1]")
+    if kv_start is not None and kv_start.shape != (ns,):
+        raise ValueError("kv_start must be [num_seqs]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    ptrs = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype),
+            _dev(v_pool, "v_pool", q.dtype), _dev(block_tables, "block_tables", torch.int32),
+            _dev(seq_lens, "seq_lens", torch.int32),
+            _dev(query_start_loc, "query_start_loc", torch.int32),
+            None if kv_start is None else _dev(kv_start, "kv_start", torch.int32))
+    if os.environ.get("PKV_CHECK") == "1":
+        pkv_check_metadata(block_tables, seq_lens, query_start_loc, kv_start, total_q, bs, nb,
+                           max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+    _raise(lib.pkv_attention_noalloc(*ptrs, ns, total_q, max_blocks, int(max_seqlen_q),
+                                     int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), dt,
+                                     _stream(q.device, stream)))
     return out
 
 

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -253,6 +254,50 @@ bool prefix_pass_pays(int num_seqs, int num_groups, int max_group_size, int max_
     return saved >= kPrefixPassMinSavedBytes;
 }
 
+// ------------------------------------------------------- static scratch
+
+// Workspace of pkv_attention_noalloc: a device array of the library's own, so
+// that a caller who cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid allocation) needs none.
+// Each GPU the library runs on holds its own copy for the life of the process.
+// In host code `scratch` names a host-side stand-in, not a device address:
+// the device address of a GPU's copy is looked up once per device, with that
+// device current, and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the copy of `scratch` on the GPU that runs `st`.
+int scratch_for_stream(hipStream_t st, void** ptr) {
+    int dev = -1;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PKV_E_HIP, "device of the stream: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKV_E_UNSUPPORTED, "device %d: static scratch is kept for devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        if (e != hipSuccess) return fail(PKV_E_HIP, "select device %d: %s", dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess || !p)
+            return fail(PKV_E_HIP, "address of the static scratch on device %d: %s", dev,
+                        hipGetErrorString(e));
+        if (back != hipSuccess)
+            return fail(PKV_E_HIP, "restore device %d: %s", cur, hipGetErrorString(back));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PKV_OK;
+}
+
 // Shared-prefix groups of a step (pkv_attention_shared_prefix).
 struct PrefixArgs {
     const int32_t* prefix_group;
@@ -270,7 +315,8 @@ int attention_impl(void* out, const void* q, const void* k_pool, const void* v_p
                    int64_t total_q, int max_blocks_per_seq, int max_seqlen_q, int max_seqlen_k,
                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                    int64_t num_blocks, float scale, pkv_dtype_t dtype, void* workspace,
-                   size_t workspace_bytes, void* stream, const PrefixArgs* pa) {
+                   size_t workspace_bytes, void* stream, const PrefixArgs* pa,
+                   bool from_scratch = false) {
     if (int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype)) return rc;
     if (num_seqs < 0) return fail(PKV_E_ARG, "num_seqs %d < 0", num_seqs);
     if (total_q < 0) return fail(PKV_E_ARG, "total_q %lld < 0", (long long)total_q);
@@ -311,6 +357,15 @@ int attention_impl(void* out, const void* q, const void* k_pool, const void* v_p
         cpl = make_cascade_plan(pl.total, num_seqs, pa->num_groups, pa->max_group_size,
                                 pa->max_prefix_len, num_q_heads, num_kv_heads, head_dim);
     const size_t need = grouped ? cpl.total : pl.total;
+    if (from_scratch) {
+        // every argument is valid: the step runs in the static scratch, if it fits
+        if (need > kScratchBytes)
+            return fail(PKV_E_WORKSPACE,
+                        "the step needs %zu bytes of workspace, above the %zu bytes of static "
+                        "scratch (use pkv_attention with a workspace)", need, kScratchBytes);
+        if (int rc = scratch_for_stream(static_cast<hipStream_t>(stream), &workspace)) return rc;
+        workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < need)
         return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                     workspace ? workspace_bytes : (size_t)0, need);
@@ -554,6 +609,19 @@ int pkv_attention(void* out, const void* q, const void* k_pool, const void* v_po
                           kv_start, num_seqs, total_q, max_blocks_per_seq, max_seqlen_q,
                           max_seqlen_k, num_q_heads, num_kv_heads, head_dim, block_size,
                           num_blocks, scale, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int pkv_attention_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, const int32_t* kv_start, int num_seqs,
+                          int64_t total_q, int max_blocks_per_seq, int max_seqlen_q,
+                          int max_seqlen_k, int num_q_heads, int num_kv_heads, int head_dim,
+                          int block_size, int64_t num_blocks, float scale, pkv_dtype_t dtype,
+                          void* stream) {
+    return attention_impl(out, q, k_pool, v_pool, block_tables, seq_lens, query_start_loc,
+                          kv_start, num_seqs, total_q, max_blocks_per_seq, max_seqlen_q,
+                          max_seqlen_k, num_q_heads, num_kv_heads, head_dim, block_size,
+                          num_blocks, scale, dtype, nullptr, 0, stream, nullptr, true);
 }
 
 size_t pkv_attention_shared_prefix_workspace_size(int num_seqs, int64_t total_q, int max_seqlen_q,

@@ -301,3 +301,35 @@ def test_shared_prefix_checker_rejects_bad_groups(mutate):
     with pytest.raises(pkv.PkvError) as e:
         pkv.pkv_check_shared_prefix(bt, lens, qsl, grp, plen, 16, 32)
     assert e.value.code == pkv.PKV_E_METADATA
+
+
+def _noalloc(lib, **over):
+    a = dict(out=FAKE, q=FAKE + 0x10000000, k=FAKE + 0x20000000, v=FAKE + 0x30000000, bt=FAKE,
+             sl=FAKE, qsl=FAKE, ks=None, num_seqs=4, total_q=4, max_blocks=8, msq=1, msk=100,
+             hq=8, hkv=2, d=128, bs=16, nb=64, scale=0.125, dtype=pkv.PKV_BF16, stream=None)
+    a.update(over)
+    return lib.pkv_attention_noalloc(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["qsl"],
+                                     a["ks"], a["num_seqs"], a["total_q"], a["max_blocks"],
+                                     a["msq"], a["msk"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                     a["nb"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=7), pkv.PKV_E_UNSUPPORTED),
+    (dict(bs=0), pkv.PKV_E_UNSUPPORTED),
+    (dict(q=None), pkv.PKV_E_ARG),
+    (dict(q=FAKE), pkv.PKV_E_ARG),                 # out aliases q
+    (dict(scale=0.0), pkv.PKV_E_ARG),
+    # valid, but its workspace (64 kv heads x 16384 sequences of pieces) is
+    # larger than the static scratch: refused before the device is touched
+    (dict(num_seqs=16384, total_q=16384, hq=64, hkv=64, msk=100,
+          k=FAKE + 0x40000000, v=FAKE + 0x80000000, q=FAKE + 0x20000000), pkv.PKV_E_WORKSPACE),
+])
+def test_noalloc_rejects_before_launching(lib, over, code):
+    assert _noalloc(lib, **over) == code
+    assert pkv.pkv_last_error() != ""
+
+
+def test_noalloc_empty_step_is_ok(lib):
+    assert _noalloc(lib, num_seqs=0) == pkv.PKV_OK
+    assert _noalloc(lib, total_q=0) == pkv.PKV_OK
