@@ -319,16 +319,38 @@ def launch_latency(reps: int = 50):
                     "synchronize"}
 
 
+def with_mixed_step(mode, fn):
+    """Runs fn with the library's mixed-step launch set to ``mode`` (fused: one
+    launch for decode waves and prefill tiles; split: separate launches)."""
+    old = os.environ.get("PKV_MIXED_STEP")
+    os.environ["PKV_MIXED_STEP"] = mode
+    try:
+        return fn()
+    finally:
+        if old is None:
+            os.environ.pop("PKV_MIXED_STEP", None)
+        else:
+            os.environ["PKV_MIXED_STEP"] = old
+
+
 def extra_prefill(steps: int, warmup: int):
     """Mixed chunked-prefill workload (16 sequences: two 512-token chunks at
-    offsets 4608 and 4601 plus 14 decodes): packed-step tokens/s, and the
-    prefill kernel alone (the two chunks as their own step) against the dense
-    bf16 matrix peak."""
+    offsets 4608 and 4601 plus 14 decodes): packed-step tokens/s with the
+    library's default launch, the same step with one launch (fused) and with
+    separate decode and prefill launches (split), and the prefill kernel alone
+    (the two chunks as their own step) against the dense bf16 matrix peak."""
     mixed = W.config_step(3, poison=False)
     sm = Step(mixed, gen_device="cuda")
     wall, attn, _, _ = time_steps(sm, steps, warmup, flush_bytes=1 << 30)
     res = {"workload": mixed.name, "packed_step_tokens_per_s": mixed.total_q / wall,
            "step_ms": wall * 1e3, "attention_ms": attn * 1e3}
+    for mode in ("fused", "split"):
+        mw, ma, _, _ = with_mixed_step(mode, lambda: time_steps(sm, steps, warmup,
+                                                                flush_bytes=1 << 30))
+        res[f"{mode}_step_ms"] = mw * 1e3
+        res[f"{mode}_attention_ms"] = ma * 1e3
+    log(f"mixed step: attention {attn * 1e3:.4f} ms (default), fused {res['fused_attention_ms']:.4f}"
+        f" ms, split {res['split_attention_ms']:.4f} ms")
     del sm
     torch.cuda.empty_cache()
     res.update(prefill_chunks(steps, warmup))
@@ -414,6 +436,8 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--mixed-step", choices=["default", "fused", "split"], default="default",
+                    help="launch form of steps with prefill chunks (for profiling one form)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the two prefill chunks of the mixed workload (for profiling)")
     args = ap.parse_args()
@@ -425,6 +449,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.manual_seed(0)
+    if args.mixed_step != "default":
+        os.environ["PKV_MIXED_STEP"] = args.mixed_step
     if args.prefill_only:
         print(json.dumps({"workload": "mixed-prefill-chunks", **prefill_chunks(args.steps, args.warmup)}),
               flush=True)
@@ -482,6 +508,18 @@ def bench_single(k, args):
                      "launch_ms_mean": attn_mean * 1e3, "launch_ms_median": attn_med * 1e3,
                      "algorithmic_bytes_per_launch": kvb},
     }
+    if k == 3:
+        # the same step with one launch (decode waves, then prefill tiles, in
+        # one grid) and with separate launches
+        modes = {}
+        for mode in ("fused", "split"):
+            mw, ma, amed, amin = with_mixed_step(mode, lambda: time_steps(step, args.steps,
+                                                                          args.warmup, flush))
+            modes[mode] = {"step_ms": mw * 1e3, "attention_ms_mean": ma * 1e3,
+                           "attention_ms_median": amed * 1e3, "attention_ms_min": amin * 1e3}
+        rec["single_launch"] = modes
+        log(f"mixed step attention: fused {modes['fused']['attention_ms_mean']:.4f} ms, split "
+            f"{modes['split']['attention_ms_mean']:.4f} ms")
     del step
     torch.cuda.empty_cache()
     if not args.no_extra and k != 3:

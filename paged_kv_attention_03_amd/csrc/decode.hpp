@@ -303,21 +303,32 @@ struct PairRegs {
     u32x4 v[2][DecodeGeom<T, D>::VCH];
 };
 
-// PS: the step has shared-prefix states to start from (a separate
-// instantiation, so that plain steps run the kernel without that code).
+// LDS of one decode wave.
+template <typename T, int D>
+struct DecodeLds {
+    __attribute__((aligned(16))) uint8_t v[2 * DecodeGeom<T, D>::PAGE_LDS];  // staged V pages
+    int32_t bid[kWindowPages];         // a window of the block-table row
+    Portion port[kWave];               // this batch's segment pieces
+    int32_t pref[kInlinePlanSeqs + 1]; // inline plan: page pairs before each sequence
+};
+
+// Decode wave number w of kDecodeWaves: streams its range of units with the
+// LDS `L` of its own.  PS: the step has shared-prefix states to start from (a
+// separate instantiation, so that plain steps run without that code).  Runs
+// as a one-wave workgroup of decode_kernel, or as one wave of a workgroup of
+// the single-launch step kernel.
 template <typename T, int D, bool PS>
-__global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, DecodeLds<T, D>& L) {
     using Gm = DecodeGeom<T, D>;
     constexpr bool kBF = !__is_same(T, float);
-    __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * Gm::PAGE_LDS];
-    __shared__ int32_t lds_bid[kWindowPages];
-    __shared__ Portion lds_port[kWave];  // this batch's segment pieces
-    __shared__ int32_t lds_pref[kInlinePlanSeqs + 1];
+    uint8_t* const lds_v = L.v;
+    int32_t* const lds_bid = L.bid;
+    Portion* const lds_port = L.port;
+    int32_t* const lds_pref = L.pref;
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int w = decode_wave_id();
     const bool inl = p.inline_plan != 0;
     const int S = p.num_seqs;
     int pb = 0, pe = 0;       // plan-kernel mode: this wave's pieces
@@ -749,6 +760,12 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
 }
 
 #undef PKV_FIELD
+
+template <typename T, int D, bool PS>
+__global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel(DecodeParams p) {
+    __shared__ DecodeLds<T, D> lds;
+    decode_wave<T, D, PS>(p, decode_wave_id(), lds);
+}
 
 // One wavefront per (sequence, query head) whose segment was cut by a wave
 // boundary, for each of the sequence's query tokens:

@@ -21,6 +21,7 @@
 #include "append.hpp"
 #include "decode.hpp"
 #include "prefill.hpp"
+#include "step.hpp"
 #include "cascade.hpp"
 #include "pool.hpp"
 
@@ -175,16 +176,38 @@ int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size
 
 // One tile per (sequence, kv head, 128/G query tokens); the grid is sized from
 // host bounds and tiles past a sequence's tokens return at once.
+long prefill_tiles(const pkv::PrefillParams& pp) {
+    return pp.state ? (long)pp.num_seqs * pp.sp_tiles
+                    : (pp.total_q + pp.tile_tokens - 1) / pp.tile_tokens + pp.num_seqs;
+}
+
+// A tile's pages: at most ceil(max_seqlen_k / 16) + 1, rounded up to pairs,
+// beyond the LDS id table (or a pool whose (page, kv head) offsets / 256
+// exceed 32 bits): the variant that reads block ids through the scalar cache.
+template <typename T, int D>
+bool prefill_long(const pkv::PrefillParams& pp) {
+    return ((long)pp.max_seqlen_k + kBlock - 1) / kBlock + 2 > pkv::kPrefillIdTable ||
+           (uint64_t)pp.num_blocks * (uint64_t)pp.Hkv * (pkv::PrefillGeom<T, D>::PAGE / 256) >
+               0xffffffffull;
+}
+
+// Whether a step with prefill sequences runs as one launch (step_kernel:
+// decode waves, then prefill tiles, in one grid) or as separate decode and
+// prefill launches.  The environment variable PKV_MIXED_STEP=fused|split
+// overrides the default.
+constexpr bool kFusedStepDefault = false;
+
+bool fused_step() {
+    const char* e = std::getenv("PKV_MIXED_STEP");
+    if (e && !std::strcmp(e, "fused")) return true;
+    if (e && !std::strcmp(e, "split")) return false;
+    return kFusedStepDefault;
+}
+
 template <typename T, int D>
 int launch_prefill(const pkv::PrefillParams& pp, hipStream_t stream, const char* what) {
-    const long tiles = pp.state ? (long)pp.num_seqs * pp.sp_tiles
-                                : (pp.total_q + pp.tile_tokens - 1) / pp.tile_tokens + pp.num_seqs;
-    // a tile's pages: at most ceil(max_seqlen_k / 16) + 1, rounded up to pairs
-    // (or a pool whose (page, kv head) offsets / 256 exceed 32 bits)
-    const bool long_ctx =
-        ((long)pp.max_seqlen_k + kBlock - 1) / kBlock + 2 > pkv::kPrefillIdTable ||
-        (uint64_t)pp.num_blocks * (uint64_t)pp.Hkv * (pkv::PrefillGeom<T, D>::PAGE / 256) >
-            0xffffffffull;
+    const long tiles = prefill_tiles(pp);
+    const bool long_ctx = prefill_long<T, D>(pp);
     if (long_ctx)
         hipLaunchKernelGGL((pkv::prefill_kernel<T, D, true>), dim3((unsigned)(tiles * pp.Hkv)),
                            dim3(pkv::PrefillGeom<T, D>::kThreads), 0, stream, pp);
@@ -203,6 +226,27 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
     if (!dp.inline_plan) {
         hipLaunchKernelGGL(pkv::decode_plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, stream, pl);
         if (int rc = hip_status("decode plan launch")) return rc;
+    }
+    if (max_seqlen_q > pl.wmax && !dp.prefix_states && fused_step()) {
+        // one launch: every workgroup runs its decode waves, then its tile
+        pkv::StepParams sp;
+        sp.dp = dp;
+        sp.pp = pp;
+        sp.prefill_wgs = (int)(prefill_tiles(pp) * pp.Hkv);
+        constexpr int kWaves = pkv::kStepWaves<T>;
+        sp.decode_per_wg = (kWaves < 8 || sp.prefill_wgs >= 2 * pkv::kDecodeWaves / 8) ? 4 : 8;
+        sp.decode_wgs = pkv::kDecodeWaves / sp.decode_per_wg;
+        const unsigned grid = (unsigned)std::max(sp.prefill_wgs, sp.decode_wgs);
+        if (prefill_long<T, D>(pp))
+            hipLaunchKernelGGL((pkv::step_kernel<T, D, true>), dim3(grid),
+                               dim3(pkv::kPrefillThreads<T>), 0, stream, sp);
+        else
+            hipLaunchKernelGGL((pkv::step_kernel<T, D, false>), dim3(grid),
+                               dim3(pkv::kPrefillThreads<T>), 0, stream, sp);
+        if (int rc = hip_status("step launch")) return rc;
+        hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)),
+                           dim3(64), 0, stream, mp);
+        return hip_status("merge launch");
     }
     if (dp.prefix_states)
         hipLaunchKernelGGL((pkv::decode_kernel<T, D, true>), dim3(pkv::kDecodeWaves), dim3(64), 0,

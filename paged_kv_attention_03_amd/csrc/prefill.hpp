@@ -218,19 +218,31 @@ __device__ __forceinline__ void unroll_rounds(F&& f) {
 // scalar data cache instead.
 constexpr int kPrefillIdTable = 4096;
 
+// LDS of one prefill workgroup: the staging ring, and (!LONG) the byte
+// offset / 256 of each staged (page, kv head) inside a pool, page-major:
+// [page of the stage (0, 1)][stage], each row padded so that reads a round
+// past the last stage stay inside it.
+constexpr int kPrefillIdRow = kPrefillIdTable / 2 + 16;
 template <typename T, int D, bool LONG>
-__global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillParams p) {
+struct PrefillLds {
+    __attribute__((aligned(1024))) uint8_t ring[PrefillGeom<T, D>::kStages * PrefillGeom<T, D>::STAGE];
+    __attribute__((aligned(8))) uint32_t bid[LONG ? 2 : 2 * kPrefillIdRow];
+};
+
+// The tile of workgroup number `block` (tile * Hkv + kv head), computed by the
+// whole workgroup with the LDS `L`.  Runs as a workgroup of prefill_kernel,
+// or as the second phase of a workgroup of the single-launch step kernel.
+template <typename T, int D, bool LONG>
+__device__ __forceinline__ void prefill_tile(const PrefillParams& p, const int block,
+                                             PrefillLds<T, D, LONG>& L) {
     using Gm = PrefillGeom<T, D>;
     constexpr bool kBF = Gm::kBF;
     constexpr int NS = Gm::kStages;
     constexpr int SPLIT = Gm::SPLIT;
     constexpr int NW = Gm::NW;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * Gm::STAGE];
-    // !LONG: byte offset / 256 of each staged (page, kv head) inside a pool,
-    // page-major: [page of the stage (0, 1)][stage], each row padded so that
-    // reads a round past the last stage stay inside it
-    constexpr int kIdRow = kPrefillIdTable / 2 + 16;
-    __shared__ __attribute__((aligned(8))) uint32_t lds_bid[LONG ? 2 : 2 * kIdRow];
+    uint8_t* const lds = L.ring;
+    constexpr int kIdRow = kPrefillIdRow;
+    uint32_t* const lds_bid = L.bid;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -242,8 +254,8 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
     // Workgroup id = tile * Hkv + kv head: workgroups are handed to the eight
     // XCDs round-robin, so with Hkv a multiple of 8 every query tile of one kv
     // head runs on one XCD and re-reads that head's K/V pages from its L2.
-    const int g = blockIdx.x % p.Hkv;
-    const int bid = blockIdx.x / p.Hkv;
+    const int g = (int)((unsigned)block % (unsigned)p.Hkv);
+    const int bid = (int)((unsigned)block / (unsigned)p.Hkv);
     const int BQ = p.tile_tokens;
 
     // ---- which sequence owns this tile: largest s with qsl[s]/BQ + s <= bid
@@ -799,6 +811,12 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillPara
             }
         }
     }
+}
+
+template <typename T, int D, bool LONG>
+__global__ void __launch_bounds__(kPrefillThreads<T>) prefill_kernel(PrefillParams p) {
+    __shared__ PrefillLds<T, D, LONG> lds;
+    prefill_tile<T, D, LONG>(p, (int)blockIdx.x, lds);
 }
 
 }  // namespace pkv
