@@ -774,7 +774,7 @@ __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel
 // the segment (waves whose unit range is empty hold nothing: they lie between
 // the segment's waves when there are fewer units than waves); maxima and sums
 // combine across lanes, then every lane sums its output elements over the
-// pieces with eight loads in flight at a time.
+// pieces that exist, eight loads in flight at a time.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) merge_kernel(MergeParams p) {
     constexpr bool kBF = !__is_same(T, float);
@@ -819,17 +819,21 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeParams p) {
             const int32_t sl = (mine ? slot_row(w) : slot_row(wa)) + column;
             const float wt = mine ? fast_exp2(p.ws_ml[(int64_t)sl * 2] - Mu) : 0.f;
             if (mine) den += wt * p.ws_ml[(int64_t)sl * 2 + 1];
-            const int nb = (int)min((int64_t)kWave, wb - w0 + 1);
-            for (int j0 = 0; j0 < nb; j0 += 8) {
+            // the lanes whose wave holds a piece, lowest first (when a step has
+            // fewer units than waves, most waves of a segment's span are empty)
+            uint64_t rem = __ballot(mine);
+            const int cnt = __popcll(rem);
+            for (int j0 = 0; j0 < cnt; j0 += 8) {
                 float o[8][PER];
                 bool use[8];
                 float wj[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    const int j = min(j0 + k, nb - 1);
+                    use[k] = rem != 0;
+                    const int j = use[k] ? __ffsll((unsigned long long)rem) - 1 : 0;
+                    rem &= rem - 1;
                     const int32_t slj = __builtin_amdgcn_readlane(sl, j);
                     wj[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
-                    use[k] = (j0 + k < nb) && __builtin_amdgcn_readlane((int)mine, j) != 0;
                     const float* src = p.ws_o + (int64_t)slj * D + lane * PER;
 #pragma unroll
                     for (int e = 0; e < PER; ++e) o[k][e] = src[e];

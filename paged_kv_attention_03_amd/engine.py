@@ -148,14 +148,23 @@ class AgentLoop:
                                                 run.num_kv_heads, run.head_dim, BLOCK_SIZE,
                                                 run.dtype)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-        # step metadata: pinned host staging, two sets used in turn (a set is
-        # refilled only after the copy that read it two steps ago completed)
+        # step metadata: one pinned host buffer and one device buffer per set
+        # (slots int64 [S] | lens int32 [S] | table int32 [S, W] | copy-on-write
+        # pairs int32 [2, S]), uploaded with one copy; two sets used in turn (a
+        # set is refilled only after the copy that read it two steps ago ended)
         W = planner.width
-        self._h = [dict(slots=torch.empty(S, dtype=torch.int64).pin_memory(),
-                        table=torch.empty((S, W), dtype=torch.int32).pin_memory(),
-                        lens=torch.empty(S, dtype=torch.int32).pin_memory(),
-                        cow=torch.empty((2, S), dtype=torch.int32).pin_memory()) for _ in range(2)]
-        self._d = [{k: torch.empty_like(v, device=dev) for k, v in h.items()} for h in self._h]
+        nbytes = 8 * S + 4 * S + 4 * S * W + 8 * S
+        self._raw = [(torch.empty(nbytes, dtype=torch.uint8).pin_memory(),
+                      torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(2)]
+
+        def views(buf):
+            o1, o2, o3 = 8 * S, 12 * S, 12 * S + 4 * S * W
+            return dict(slots=buf[:o1].view(torch.int64), lens=buf[o1:o2].view(torch.int32),
+                        table=buf[o2:o3].view(torch.int32).view(S, W),
+                        cow=buf[o3:].view(torch.int32).view(2, S))
+
+        self._h = [views(h) for h, _ in self._raw]
+        self._d = [views(d) for _, d in self._raw]
         self._ev = [None, None]
         torch.cuda.synchronize()
 
@@ -172,14 +181,13 @@ class AgentLoop:
         h["slots"].numpy()[:] = plan.slots
         h["table"].numpy()[:] = plan.table
         h["lens"].numpy()[:] = plan.lens
-        d["slots"].copy_(h["slots"], non_blocking=True)
-        d["table"].copy_(h["table"], non_blocking=True)
-        d["lens"].copy_(h["lens"], non_blocking=True)
-        if plan.copies:
-            n = len(plan.copies)
+        n = len(plan.copies)
+        if n:
             h["cow"].numpy()[:, :n] = np.array(plan.copies, dtype=np.int32).T
-            d["cow"].copy_(h["cow"], non_blocking=True)
-            pkv_copy_blocks(self.kp, self.vp, d["cow"][0, :n], d["cow"][1, :n])
+        self._raw[b][1].copy_(self._raw[b][0], non_blocking=True)
+        if n:
+            pkv_copy_blocks(self.kp, self.vp, d["cow"][0, :n].contiguous(),
+                            d["cow"][1, :n].contiguous())
         e = torch.cuda.Event()
         e.record()
         self._ev[b] = e
