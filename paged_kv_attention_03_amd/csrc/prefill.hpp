@@ -483,7 +483,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, const int b
     // [kv_start, pos_max].  The running max is raised lazily: only when some
     // column's tile max exceeds it by more than 8 (log2 units); column sums of
     // P come from one extra MFMA against an all-ones operand.
-    auto compute = [&](auto edge_tag, auto slot_tag, int dyn_slot, int st) {
+    // `after_qk` runs once the logit products are issued (it reads the next
+    // round's page offsets).
+    auto compute = [&](auto edge_tag, auto slot_tag, int dyn_slot, int st, auto&& after_qk) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         constexpr int SLOT = decltype(slot_tag)::value;
         // slots from 64 KiB on use the offsets 64 KiB up and a smaller base
@@ -492,8 +494,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, const int b
         const int* ko = HI ? koff_hi : koff;
         const int* vo = HI ? voff_hi : voff;
         const int pa = first_page + 2 * st;
-        // ---- operands from LDS: K for the logits, and (bfloat16) V^T for the
-        // product, read up front so their latency overlaps the softmax
+        // ---- operands from LDS: K for the logits first.  The (bfloat16) V^T
+        // operands are read only once the logit products are issued: right
+        // after the barrier every wavefront of the workgroup reads its K, and
+        // with the V^T reads queued behind them the second wavefront of a
+        // SIMD would wait for the first one's V^T before its own K arrived.
+        // Read later, their latency overlaps the softmax.
         u32x4 kop[2][Gm::KCH];
 #pragma unroll
         for (int x = 0; x < 2; ++x)
@@ -501,14 +507,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, const int b
             for (int i = 0; i < Gm::KCH; ++i)
                 kop[x][i] = *reinterpret_cast<const u32x4*>(sb + x * Gm::PAGE + ko[i]);
         u32x4 vop[kBF ? Gm::NT : 1];
-        if constexpr (kBF) {
-#pragma unroll
-            for (int t = 0; t < Gm::NT; ++t) {
-                const uint2 lo = lds_read_tr16(sb + 2 * Gm::PAGE + vo[t]);
-                const uint2 hi = lds_read_tr16(sb + 3 * Gm::PAGE + vo[t]);
-                vop[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
-            }
-        }
         mfma_priority(1);
         // ---- S^T tiles: keys of page x as rows, this wavefront's rows as columns.
         // The four tiles accumulate over the head dimension in four independent
@@ -541,6 +539,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, const int b
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (kBF) {
+#pragma unroll
+            for (int t = 0; t < Gm::NT; ++t) {
+                const uint2 lo = lds_read_tr16(sb + 2 * Gm::PAGE + vo[t]);
+                const uint2 hi = lds_read_tr16(sb + 3 * Gm::PAGE + vo[t]);
+                vop[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        }
+        after_qk();
         mfma_priority(0);
         bool kval[8];
         if constexpr (EDGE) {
@@ -686,18 +693,26 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, const int b
                     ids[j] = stage_ids(nx);  // inside the padded row; used only if it exists
                 }
             }
-            if constexpr (!EDGE && kOnePage && SPLIT == 2) {
-                // both stages of the next round in one read (an even index)
-                const uint2 o =
-                    *reinterpret_cast<const uint2*>(&lds_bid[pw * kIdRow + rr * SPLIT + NS]);
-                const int a = __builtin_amdgcn_readfirstlane((int)o.x);
-                const int b = __builtin_amdgcn_readfirstlane((int)o.y);
-                ids[0] = int2{a, a};
-                ids[1] = int2{b, b};
-            }
         }
+        // Interior rounds of the one-page layout read both stages of the next
+        // round in one 8-byte read (an even index), issued after this round's
+        // logit products and made scalar at the end of the round, so that its
+        // LDS round trip never sits between the barrier and the K reads.
+        constexpr bool kLateIds = !LONG && !EDGE && kOnePage && SPLIT == 2;
+        uint2 next_ids;
+        auto after_qk = [&]() {
+            if constexpr (kLateIds)
+                next_ids = *reinterpret_cast<const uint2*>(&lds_bid[pw * kIdRow + rr * SPLIT + NS]);
+        };
+        // (every stage of an interior round exists)
         const int st = rr * SPLIT + half;
-        if (st < nstage) compute(edge_tag, slot_tag, (rr * SPLIT) % NS, st);
+        if (!EDGE || st < nstage) compute(edge_tag, slot_tag, (rr * SPLIT) % NS, st, after_qk);
+        if constexpr (kLateIds) {
+            const int a = __builtin_amdgcn_readfirstlane((int)next_ids.x);
+            const int b = __builtin_amdgcn_readfirstlane((int)next_ids.y);
+            ids[0] = int2{a, a};
+            ids[1] = int2{b, b};
+        }
         if constexpr (LONG) {
             // the next round's block ids, fetched after this round's LDS reads
             // so that their scalar-cache latency overlaps the barrier rather
