@@ -116,8 +116,8 @@ def to_f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def check_close(got, ref, dtype, what, quiet=False):
-    atol, rtol = TOL[dtype]
+def check_close(got, ref, dtype, what, quiet=False, tol_scale=1.0):
+    atol, rtol = (t * tol_scale for t in TOL[dtype])
     g = to_f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     ok, maxerr = close(g, ref, atol, rtol)
     denom = float(np.linalg.norm(ref)) or 1.0

@@ -5,7 +5,8 @@ page edges and across several splits, speculative-verify windows of up to
 context, mixed steps, left-padded steps; plus bitwise
 properties of the GPU path itself (physical page placement, run-to-run
 determinism, shared versus duplicated prefix pages) and a large packed step
-checked on sampled tokens.  Pools are NaN outside the valid rows."""
+checked on sampled tokens; a step with 8x and 16x queries (sharp softmax rows)
+pins the logit precision.  Pools are NaN outside the valid rows."""
 import numpy as np
 import pytest
 import torch
@@ -20,16 +21,18 @@ DTYPES = [torch.float32, torch.bfloat16]
 EDGE_LENS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 1000]
 
 
-def _run_full(st, what):
-    """GPU step vs the oracle on the whole step; also the pool bytes."""
-    q = st.make_q("cpu")
+def _run_full(st, what, q_mul=1.0, tol_scale=1.0):
+    """GPU step vs the oracle on the whole step; also the pool bytes.  ``q_mul``
+    (a power of two, so exact in both dtypes) scales the queries, ``tol_scale``
+    the tolerance."""
+    q = st.make_q("cpu") * q_mul
     kp, vp = gpu_pools(st, "cpu")
     okp, ovp = oracle_pools(st)
     assert np.array_equal(raw_bits(kp), okp.view(raw_bits(kp).dtype)), "K pool bytes differ"
     assert np.array_equal(raw_bits(vp), ovp.view(raw_bits(vp).dtype)), "V pool bytes differ"
     out = gpu_attention(st, q.cuda(), kp, vp)
     ref = oracle_step(st, q, pools=(okp, ovp))
-    check_close(out, ref, st.dtype, what)
+    check_close(out, ref, st.dtype, what, tol_scale=tol_scale)
     return out
 
 
@@ -58,6 +61,32 @@ def test_prefill_and_mixed_sweep(G, D, dtype):
     lens = [b for _, b in PREFILL_SHAPES]
     st = W.build_step("prefill-sweep", lens, ql, 2 * G, 2, D, dtype, 200 + G * 7 + D)
     _run_full(st, f"prefill G={G} D={D}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("q_mul", [8.0, 16.0])
+def test_sharp_softmax_step(q_mul, dtype):
+    """Queries 8x and 16x larger than N(0, 1): logits of tens, so most rows put
+    nearly all their weight on a few keys and an error in a logit shows in the
+    output almost undamped.  A kernel that rounded the scaled queries (or the
+    logits) to bfloat16 before the exponential fails the bfloat16 case (max
+    error ~0.09 at 8x against ~0.015 for exact logits), while ordinary inputs
+    hide it.  Decodes, verify windows and chunks with cached context, G 4,
+    D 128.
+
+    The bfloat16 bound is the usual 1e-2.  The float32 bound of 1e-5 holds for
+    logits of order one: a float32 logit carries a rounding error in proportion
+    to its magnitude, and the softmax passes it on as a relative error of the
+    weights, so the float32 bound is scaled by the query factor (a plain
+    float32 softmax attention on the host misses 1e-5 on these inputs by
+    2.8x at 8x and 4.4x at 16x, the GPU path by 2.5x and 4.0x)."""
+    log(f"sharp softmax q x{q_mul} {dtype}")
+    lens = [900, 300, 2000, 77, 1500, 1640, 33, 4097]
+    ql = [1, 3, 128, 1, 4, 700, 2, 1000]
+    st = W.build_step("sharp-softmax", lens, ql, 16, 4, 128, dtype, 260 + int(q_mul))
+    _run_full(st, f"sharp softmax q x{q_mul}", q_mul=q_mul,
+              tol_scale=q_mul if dtype == torch.float32 else 1.0)
 
 
 WINDOW_LENS = [2, 15, 16, 17, 31, 33, 64, 65, 100, 257, 1000, 1600]
