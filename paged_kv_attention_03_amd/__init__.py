@@ -26,7 +26,8 @@ __all__ = [
     "pkv_attention_workspace_size", "pkv_attention_noalloc", "pkv_attention_shared_prefix",
     "pkv_attention_shared_prefix_workspace_size", "pkv_check_shared_prefix",
     "pkv_check_metadata", "pkv_check_slots", "pkv_last_error",
-    "pkv_copy_blocks", "PagePool", "library_path", "load_library",
+    "pkv_copy_blocks", "PagePool", "library_path", "load_library", "PreparedCall",
+    "prepare_append", "prepare_attention",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -162,11 +163,29 @@ def _stream(device: torch.device, stream) -> int:
     return int(getattr(stream, "cuda_stream", stream))
 
 
-def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
-               v_pool: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
-    """Write new K/V rows [T, Hkv, D] into pools [num_blocks, Hkv, bs, D] at
-    ``slot_mapping`` [T] (int64; negative = skip)."""
-    lib = load_library()
+class PreparedCall:
+    """One library call whose arguments were checked and converted once.
+    Calling the object issues the same C call again: the same device
+    pointers, sizes and stream, so the tensors it was prepared with must stay
+    alive and keep their storage (the object holds references to them); their
+    contents may change between calls.  The host-side metadata checks that
+    ``PKV_CHECK=1`` turns on for the plain calls do not run here."""
+
+    __slots__ = ("_fn", "_args", "_keep", "out")
+
+    def __init__(self, fn, args, keep, out=None):
+        self._fn = fn
+        self._args = tuple(a if a is None else t(a) for t, a in zip(fn.argtypes, args))
+        self._keep = keep
+        self.out = out
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != PKV_OK:
+            raise PkvError(rc, pkv_last_error())
+
+
+def _append_args(k_new, v_new, k_pool, v_pool, slot_mapping, stream):
     dt = _dtype_code(k_pool.dtype)
     if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("pools must be [num_blocks, Hkv, block_size, D] and equal")
@@ -179,9 +198,29 @@ def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
     args = (_dev(k_new, "k_new", k_pool.dtype), _dev(v_new, "v_new", k_pool.dtype),
             _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
             _dev(slot_mapping, "slot_mapping", torch.int64))
+    return args + (t, hkv, d, bs, nb, dt, _stream(k_pool.device, stream))
+
+
+def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+               v_pool: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write new K/V rows [T, Hkv, D] into pools [num_blocks, Hkv, bs, D] at
+    ``slot_mapping`` [T] (int64; negative = skip)."""
+    lib = load_library()
+    args = _append_args(k_new, v_new, k_pool, v_pool, slot_mapping, stream)
     if os.environ.get("PKV_CHECK") == "1":
-        pkv_check_slots(slot_mapping, bs, nb)
-    _raise(lib.pkv_append(*args, t, hkv, d, bs, nb, dt, _stream(k_pool.device, stream)))
+        pkv_check_slots(slot_mapping, k_pool.shape[2], k_pool.shape[0])
+    _raise(lib.pkv_append(*args))
+
+
+def prepare_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+                   v_pool: torch.Tensor, slot_mapping: torch.Tensor,
+                   stream=None) -> PreparedCall:
+    """``pkv_append`` on these tensors, checked once; each call of the result
+    re-issues it (on ``stream``, else the current stream at preparation)."""
+    lib = load_library()
+    return PreparedCall(lib.pkv_append,
+                        _append_args(k_new, v_new, k_pool, v_pool, slot_mapping, stream),
+                        (k_new, v_new, k_pool, v_pool, slot_mapping))
 
 
 def pkv_attention_workspace_size(num_seqs: int, total_q: int, max_seqlen_q: int,
@@ -205,6 +244,21 @@ def pkv_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     kv_start [S] int32 or None.  ``max_seqlen_q``/``max_seqlen_k`` are host
     upper bounds.  Returns ``out`` [total_q, Hq, D] (allocated if None)."""
     lib = load_library()
+    args, out, workspace = _attention_args(q, k_pool, v_pool, block_tables, seq_lens,
+                                           query_start_loc, scale, max_seqlen_q, max_seqlen_k,
+                                           kv_start, out, workspace, stream)
+    if os.environ.get("PKV_CHECK") == "1":
+        pkv_check_metadata(block_tables, seq_lens, query_start_loc, kv_start, q.shape[0],
+                           k_pool.shape[2], k_pool.shape[0], max_seqlen_q=max_seqlen_q,
+                           max_seqlen_k=max_seqlen_k)
+    _raise(lib.pkv_attention(*args))
+    return out
+
+
+def _attention_args(q, k_pool, v_pool, block_tables, seq_lens, query_start_loc, scale,
+                    max_seqlen_q, max_seqlen_k, kv_start, out, workspace, stream):
+    """Checks the tensors of an attention call and returns (C arguments, out,
+    workspace), allocating ``out`` and the workspace when not given."""
     dt = _dtype_code(q.dtype)
     if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [total_q, Hq, D] and pools [num_blocks, Hkv, bs, D]")
@@ -234,13 +288,29 @@ def pkv_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
             _dev(seq_lens, "seq_lens", torch.int32),
             _dev(query_start_loc, "query_start_loc", torch.int32),
             None if kv_start is None else _dev(kv_start, "kv_start", torch.int32))
-    if os.environ.get("PKV_CHECK") == "1":
-        pkv_check_metadata(block_tables, seq_lens, query_start_loc, kv_start, total_q, bs, nb,
-                           max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
-    _raise(lib.pkv_attention(*ptrs, ns, total_q, max_blocks, int(max_seqlen_q), int(max_seqlen_k),
-                             hq, hkv, d, bs, nb, float(scale), dt, ws_ptr, ws_bytes,
-                             _stream(q.device, stream)))
-    return out
+    args = ptrs + (ns, total_q, max_blocks, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs,
+                   nb, float(scale), dt, ws_ptr, ws_bytes, _stream(q.device, stream))
+    return args, out, workspace
+
+
+def prepare_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                      query_start_loc: torch.Tensor, scale: float, *, max_seqlen_q: int,
+                      max_seqlen_k: int, kv_start: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
+    """``pkv_attention`` on these tensors, checked once (``out`` and the
+    workspace are allocated here when not given; ``.out`` of the result is
+    the output tensor); each call of the result re-issues it with the current
+    contents of the metadata tensors, which must stay within the same host
+    bounds (``max_seqlen_q``, ``max_seqlen_k``)."""
+    lib = load_library()
+    args, out, workspace = _attention_args(q, k_pool, v_pool, block_tables, seq_lens,
+                                           query_start_loc, scale, max_seqlen_q, max_seqlen_k,
+                                           kv_start, out, workspace, stream)
+    return PreparedCall(lib.pkv_attention, args, (q, k_pool, v_pool, block_tables, seq_lens,
+                                                  query_start_loc, kv_start, out, workspace),
+                        out=out)
 
 
 def pkv_attention_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

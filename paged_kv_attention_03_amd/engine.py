@@ -13,7 +13,11 @@ attention through the tables ("Replacing attention, reusing the rest").
 prefix, one ``append_batch`` per step, block-table export).  ``AgentLoop``
 owns the device pools and runs each step: metadata upload, any copy-on-write
 page copies (``pkv_copy_blocks``), ``pkv_append`` of the step's rows, then
-``pkv_attention``.  Neither holds any attention arithmetic.
+``pkv_attention``.  With ``graphs`` the device part of every step (metadata
+upload, append, attention) is captured once in a HIP graph and replayed
+after the step's planning on the host, as an engine captures its decode
+step: the launches then cost one graph launch of host time instead of one
+binding call each.  Neither holds any attention arithmetic.
 """
 from __future__ import annotations
 
@@ -25,7 +29,8 @@ import numpy as np
 import torch
 
 from . import PagePool, pkv_append, pkv_attention, pkv_attention_shared_prefix, \
-    pkv_attention_shared_prefix_workspace_size, pkv_attention_workspace_size, pkv_copy_blocks
+    pkv_attention_shared_prefix_workspace_size, pkv_attention_workspace_size, pkv_copy_blocks, \
+    prepare_append, prepare_attention
 
 BLOCK_SIZE = 16
 
@@ -105,11 +110,21 @@ class AgentLoop:
     Every row the run will append is generated on ``gen_device`` up front (the
     model's projections would produce them; they are inputs), so a step's
     device work is the upload of its metadata, the append and attention.
-    Pool bytes no row was written to hold NaN when ``poison``."""
+    Pool bytes no row was written to hold NaN when ``poison``.
+
+    ``lookahead`` K: the host plans K steps at a time and uploads their
+    metadata with one copy (a decode step appends one token per sequence
+    whatever the token is, so its slots and block tables are known before the
+    steps ahead of it run); each step then launches its own append and
+    attention.  ``graphs`` (with K = 1): each step's upload, append and
+    attention are one captured HIP graph, replayed after its planning."""
 
     def __init__(self, run, planner: AgentPlanner, *, poison: bool = True, gen_device="cuda",
-                 prefix_pass: Optional[str] = None):
+                 prefix_pass: Optional[str] = None, graphs: bool = False, lookahead: int = 1):
+        if lookahead < 1 or (graphs and lookahead != 1):
+            raise ValueError("lookahead must be >= 1, and 1 with graphs")
         self.run, self.plan = run, planner
+        self.K = lookahead
         dev = torch.device("cuda")
         shape = (planner.num_blocks, run.num_kv_heads, BLOCK_SIZE, run.head_dim)
         fill = float("nan") if poison else 0.0
@@ -148,53 +163,74 @@ class AgentLoop:
                                                 run.num_kv_heads, run.head_dim, BLOCK_SIZE,
                                                 run.dtype)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-        # step metadata: one pinned host buffer and one device buffer per set
-        # (slots int64 [S] | lens int32 [S] | table int32 [S, W] | copy-on-write
-        # pairs int32 [2, S]), uploaded with one copy; two sets used in turn (a
-        # set is refilled only after the copy that read it two steps ago ended)
+        # step metadata, one set per step (slots int64 [S] | lens int32 [S] |
+        # table int32 [S, W] | copy-on-write pairs int32 [2, S]); two halves of
+        # K sets, each a pinned host buffer and a device buffer uploaded with
+        # one copy, used by alternate groups of K steps (a half is refilled
+        # only after the copy that read it two groups ago ended)
         W = planner.width
         nbytes = 8 * S + 4 * S + 4 * S * W + 8 * S
-        self._raw = [(torch.empty(nbytes, dtype=torch.uint8).pin_memory(),
-                      torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(2)]
+        nbytes = (nbytes + 255) // 256 * 256
+        self._raw = [(torch.empty(self.K * nbytes, dtype=torch.uint8).pin_memory(),
+                      torch.empty(self.K * nbytes, dtype=torch.uint8, device=dev))
+                     for _ in range(2)]
 
-        def views(buf):
+        def views(buf, k):
+            b = buf[k * nbytes:(k + 1) * nbytes]
             o1, o2, o3 = 8 * S, 12 * S, 12 * S + 4 * S * W
-            return dict(slots=buf[:o1].view(torch.int64), lens=buf[o1:o2].view(torch.int32),
-                        table=buf[o2:o3].view(torch.int32).view(S, W),
-                        cow=buf[o3:].view(torch.int32).view(2, S))
+            return dict(slots=b[:o1].view(torch.int64), lens=b[o1:o2].view(torch.int32),
+                        table=b[o2:o3].view(torch.int32).view(S, W),
+                        cow=b[o3:o3 + 8 * S].view(torch.int32).view(2, S))
 
-        self._h = [views(h) for h, _ in self._raw]
-        self._d = [views(d) for _, d in self._raw]
+        self._h = [[views(h, k) for k in range(self.K)] for h, _ in self._raw]
+        self._d = [[views(d, k) for k in range(self.K)] for _, d in self._raw]
         self._ev = [None, None]
+        self._ev_obj = [torch.cuda.Event(), torch.cuda.Event()]
+        self._chunk = []
+        self._graphs = None
+        # each step's append and attention, checked once, on its metadata set
+        self._app, self._att = [], []
+        for i in range(run.steps):
+            d = self._set(self._d, i)
+            self._app.append(prepare_append(self.step_k[i], self.step_v[i], self.kp, self.vp,
+                                            d["slots"]))
+            if prefix_pass is None:
+                self._att.append(prepare_attention(
+                    self.step_q[i], self.kp, self.vp, d["table"], d["lens"], self.qsl,
+                    run.scale, max_seqlen_q=1, max_seqlen_k=run.max_seqlen_k, out=self.out,
+                    workspace=self.ws))
         torch.cuda.synchronize()
+        if graphs:
+            self._capture()
 
-    def step(self, i: int, ev=None) -> torch.Tensor:
-        """Runs decode step i (host planning, upload, copies, append,
-        attention) and returns ``out`` [S, Hq, D] (overwritten by the next
-        step).  ``ev``: optional (start, end) CUDA events around attention."""
-        run = self.run
-        plan = self.plan.step(i)
-        b = i % 2
-        if self._ev[b] is not None:
-            self._ev[b].synchronize()
-        h, d = self._h[b], self._d[b]
-        h["slots"].numpy()[:] = plan.slots
-        h["table"].numpy()[:] = plan.table
-        h["lens"].numpy()[:] = plan.lens
+    def _set(self, sets, i: int):
+        """Metadata set of step i: half (i // K) % 2, entry i % K."""
+        c, k = divmod(i, self.K)
+        return sets[c % 2][k]
+
+    def _upload(self, h: int):
+        self._raw[h][1].copy_(self._raw[h][0], non_blocking=True)
+
+    def _fill(self, hs, plan: StepPlan):
+        hs["slots"].numpy()[:] = plan.slots
+        hs["table"].numpy()[:] = plan.table
+        hs["lens"].numpy()[:] = plan.lens
         n = len(plan.copies)
         if n:
-            h["cow"].numpy()[:, :n] = np.array(plan.copies, dtype=np.int32).T
-        self._raw[b][1].copy_(self._raw[b][0], non_blocking=True)
-        if n:
-            pkv_copy_blocks(self.kp, self.vp, d["cow"][0, :n].contiguous(),
-                            d["cow"][1, :n].contiguous())
-        e = torch.cuda.Event()
-        e.record()
-        self._ev[b] = e
-        pkv_append(self.step_k[i], self.step_v[i], self.kp, self.vp, d["slots"])
+            hs["cow"].numpy()[:, :n] = np.array(plan.copies, dtype=np.int32).T
+
+    def _compute(self, i: int, ev=None, prepared: bool = True):
+        """Append of step i's rows and attention, on its metadata set."""
+        run, d = self.run, self._set(self._d, i)
+        if prepared:
+            self._app[i]()
+        else:
+            pkv_append(self.step_k[i], self.step_v[i], self.kp, self.vp, d["slots"])
         if ev is not None:
             ev[0].record()
-        if self.prefix_pass is not None:
+        if prepared and self._att:
+            self._att[i]()
+        elif self.prefix_pass is not None:
             pkv_attention_shared_prefix(
                 self.step_q[i], self.kp, self.vp, d["table"], d["lens"], self.qsl, run.scale,
                 self.group, self.plen, max_group_size=run.num_seqs,
@@ -206,4 +242,70 @@ class AgentLoop:
                           workspace=self.ws)
         if ev is not None:
             ev[1].record()
+
+    def _capture(self):
+        """One graph per step index: upload of the step's metadata half (K is
+        1: the host fills its pinned half before the replay), append and
+        attention, all on the capturing stream (plain calls: prepared ones
+        hold the stream they were prepared on).  A warm-up per half first, on
+        metadata that is valid as it stands: every slot -1 (the append writes
+        nothing) and the block tables and lengths the pool holds after the
+        prompts."""
+        run, S = self.run, self.run.num_seqs
+        table, lens = self.plan.pool.block_tables(list(range(S)), self.plan.width)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for h in range(2):
+                hs = self._h[h][0]
+                hs["slots"].numpy()[:] = -1
+                hs["table"].numpy()[:] = table
+                hs["lens"].numpy()[:] = lens
+                self._upload(h)
+                self._compute(h, prepared=False)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self._graphs = []
+        for i in range(run.steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._upload(i % 2)
+                self._compute(i, prepared=False)
+            self._graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(self, i: int, ev=None) -> torch.Tensor:
+        """Runs decode step i (host planning, upload, copies, append,
+        attention) and returns ``out`` [S, Hq, D] (overwritten by the next
+        step).  ``ev``: optional (start, end) CUDA events around attention.
+        Steps run in order from 0."""
+        c, k = divmod(i, self.K)
+        h = c % 2
+        if k == 0:
+            # plan this group of steps and upload its metadata
+            if self._ev[h] is not None:
+                self._ev[h].synchronize()
+            last = min(i + self.K, self.run.steps)
+            self._chunk = [self.plan.step(j) for j in range(i, last)]
+            for kk, plan in enumerate(self._chunk):
+                self._fill(self._h[h][kk], plan)
+            if self._graphs is not None and not self._chunk[0].copies:
+                if ev is not None:
+                    raise ValueError("per-call events are not available in graph mode")
+                self._graphs[i].replay()
+                e = self._ev_obj[h]
+                e.record()
+                self._ev[h] = e
+                return self.out
+            self._upload(h)
+            e = self._ev_obj[h]
+            e.record()
+            self._ev[h] = e
+        plan = self._chunk[k]
+        n = len(plan.copies)
+        if n:  # (in graph mode such a step runs eagerly: the copies land before the append)
+            d = self._d[h][k]
+            pkv_copy_blocks(self.kp, self.vp, d["cow"][0, :n].contiguous(),
+                            d["cow"][1, :n].contiguous())
+        self._compute(i, ev)
         return self.out

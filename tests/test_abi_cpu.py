@@ -216,6 +216,37 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         pkv.pkv_append(x, x, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
                        torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        pkv.prepare_append(x, x, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
+                           torch.zeros(4, dtype=torch.int64))
+    q = torch.zeros(4, 8, 64)
+    with pytest.raises(ValueError):
+        pkv.prepare_attention(q, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
+                              torch.zeros(4, 2, dtype=torch.int32),
+                              torch.ones(4, dtype=torch.int32),
+                              torch.arange(5, dtype=torch.int32), 0.125, max_seqlen_q=1,
+                              max_seqlen_k=1, out=q, workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def test_prepared_call_converts_once_and_reports_errors(lib):
+    """A prepared call hands the C function the same converted arguments on
+    every call and turns a non-zero status into PkvError."""
+    seen = []
+
+    def fn(*args):
+        seen.append(args)
+        return pkv.PKV_OK if len(seen) == 1 else pkv.PKV_E_ARG
+
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                   ctypes.c_float]
+    call = pkv.PreparedCall(fn, (0x10000, None, 7, 1 << 40, 0.5), keep=())
+    call()
+    a = seen[0]
+    assert isinstance(a[0], ctypes.c_void_p) and a[0].value == 0x10000 and a[1] is None
+    assert a[2].value == 7 and a[3].value == 1 << 40 and a[4].value == 0.5
+    with pytest.raises(pkv.PkvError):
+        call()
+    assert seen[1] == seen[0]
 
 
 # ------------------------------------------------------- shared-prefix steps

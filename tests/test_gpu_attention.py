@@ -220,6 +220,40 @@ def test_long_context_prefill_chunk(dtype):
 
 
 @pytest.mark.gpu
+def test_prepared_calls_match_the_plain_calls():
+    """prepare_append / prepare_attention re-issue the same C calls: pools and
+    outputs bitwise equal to pkv_append / pkv_attention on the mixed step, also
+    after the tensors' contents change in place between calls."""
+    st = W.config_step(3)
+    log("prepared calls on the mixed step")
+    q = st.make_q("cpu").cuda()
+    # the step's rows into NaN pools, by the plain and the prepared call
+    k_new, v_new, slots = st.rows("step", "cuda", gen_device="cpu")
+    ka, va = st.new_pool("cuda", poison=True)
+    kb, vb = ka.clone(), va.clone()
+    before = raw_bits(kb).copy()
+    pkv.pkv_append(k_new, v_new, ka, va, slots)
+    app = pkv.prepare_append(k_new, v_new, kb, vb, slots)
+    app()
+    torch.cuda.synchronize()
+    assert not np.array_equal(raw_bits(kb), before), "the prepared append wrote nothing"
+    assert np.array_equal(raw_bits(kb), raw_bits(ka)) and np.array_equal(raw_bits(vb), raw_bits(va))
+    del ka, va, kb, vb
+    kp, vp = gpu_pools(st, "cpu")
+    md = st.metadata("cuda")
+    att = pkv.prepare_attention(q, kp, vp, md["block_tables"], md["seq_lens"],
+                                md["query_start_loc"], st.scale, max_seqlen_q=st.max_seqlen_q,
+                                max_seqlen_k=st.max_seqlen_k, kv_start=md["kv_start"])
+    for rep in range(2):
+        if rep:
+            q.mul_(0.5)  # new contents, same storage
+        want = raw_bits(gpu_attention(st, q, kp, vp)).copy()
+        att()
+        torch.cuda.synchronize()
+        assert np.array_equal(raw_bits(att.out), want), f"rep {rep}"
+
+
+@pytest.mark.gpu
 def test_workspace_reuse_and_explicit_out():
     st = W.config_step(2)
     q = st.make_q("cpu").cuda()

@@ -93,6 +93,42 @@ def test_config4_agent_loop(dtype):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("mode", [dict(graphs=True), dict(lookahead=8)],
+                         ids=["graph-replayed", "lookahead-8"])
+def test_config4_agent_loop_other_launch_forms(mode):
+    """The same loop with each step's device work (metadata upload, append,
+    attention) captured once in a HIP graph and replayed after the host's
+    planning, or with the host planning 8 steps at a time and uploading their
+    metadata in one copy (70 steps: the last group holds 6): every step's
+    output and the final pools bitwise equal to the step-by-step loop's, and
+    the first and last steps against the oracle."""
+    run = W.AgentRun()
+    p_eager, p_graph = AgentPlanner(run), AgentPlanner(run)
+    eager = AgentLoop(run, p_eager, poison=True, gen_device="cpu")
+    graph = AgentLoop(run, p_graph, poison=True, gen_device="cpu", **mode)
+    log(f"config 4 agent loop, step by step and {mode}, pages={p_eager.num_blocks}")
+    okp, ovp, obt = contiguous_pool([(k.cpu(), v.cpu()) for k, v in eager.rows],
+                                    run.num_kv_heads, run.head_dim, run.dtype)
+    qsl = np.arange(run.num_seqs + 1, dtype=np.int32)
+    for i in range(run.steps):
+        a = raw_bits(eager.step(i)).copy()
+        g = graph.step(i)
+        torch.cuda.synchronize()
+        assert np.array_equal(raw_bits(g), a), f"step {i}: {mode} != step by step"
+        if i in (0, run.steps - 1):
+            ref = oracle.oracle_attention(run.step_q(i, "cpu"), okp, ovp, obt, run.seq_lens_at(i),
+                                          qsl, run.scale)
+            check_close(g, ref, run.dtype, f"graph step {i}")
+    assert np.array_equal(raw_bits(graph.kp), raw_bits(eager.kp)), "K pools differ"
+    assert np.array_equal(raw_bits(graph.vp), raw_bits(eager.vp)), "V pools differ"
+    log(f"  all {run.steps} steps bitwise equal to the step-by-step loop")
+    p_eager.close()
+    p_graph.close()
+    del eager, graph
+    _free()
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32-shadow"])
 def test_config5_large_decode_ragged_and_padded(dtype):
     """All 128 sequences, every head, of both the ragged and the left-padded
