@@ -106,6 +106,11 @@ struct DecodeParams {
     // inline-plan mode (num_seqs <= kInlinePlanSeqs): every wave derives its
     // pieces from the step metadata; wave 0 also writes pair_prefix
     int inline_plan;
+    // inline-plan mode only: wave w (= workgroup w, num_seqs * Hkv of them)
+    // takes the whole segment of kv head w / num_seqs and sequence
+    // w % num_seqs instead of an even share of the units, so no segment is
+    // cut and no merge follows (steps whose segments are all short)
+    int whole_segments;
     const int32_t* seq_lens;
     const int32_t* qsl;
     const int32_t* kv_start;
@@ -360,9 +365,18 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
         wave_lds_fence();
         if (w == 0)
             for (int s = lane; s <= S; s += kWave) p.pair_prefix[s] = lds_pref[s];
-        const int64_t U = (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(lds_pref[S]);
-        u0 = wave_start(w, U);
-        u1 = wave_start(w + 1, U);
+        const int32_t P_S = __builtin_amdgcn_readfirstlane(lds_pref[S]);
+        if (p.whole_segments) {
+            const int g = w / S, s = w - (w / S) * S;
+            if (g >= p.Hkv) return;
+            u0 = segment_start(g, __builtin_amdgcn_readfirstlane(lds_pref[s]), P_S);
+            u1 = u0 + (__builtin_amdgcn_readfirstlane(lds_pref[s + 1]) -
+                       __builtin_amdgcn_readfirstlane(lds_pref[s]));
+        } else {
+            const int64_t U = (int64_t)p.Hkv * P_S;
+            u0 = wave_start(w, U);
+            u1 = wave_start(w + 1, U);
+        }
         if (u0 >= u1) return;
     } else {
         pb = p.portion_begin[w];
@@ -764,7 +778,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
 template <typename T, int D, bool PS>
 __global__ void __launch_bounds__(64, __is_same(T, float) ? 1 : 2) decode_kernel(DecodeParams p) {
     __shared__ DecodeLds<T, D> lds;
-    decode_wave<T, D, PS>(p, decode_wave_id(), lds);
+    decode_wave<T, D, PS>(p, p.whole_segments ? (int)blockIdx.x : decode_wave_id(), lds);
 }
 
 // One wavefront per (sequence, query head) whose segment was cut by a wave

@@ -204,6 +204,23 @@ bool fused_step() {
     return kFusedStepDefault;
 }
 
+// Whether a decode-only step runs one wave per (sequence, kv head) segment
+// (no segment cut, no merge launch) instead of spreading the units evenly
+// over kDecodeWaves waves.  Chosen when every segment is short (the host
+// bound max_seqlen_k) and there are no more segments than waves: a short
+// segment streams in a few page-pair round trips, less than the merge launch
+// that cutting it would need.  PKV_DECODE_SEGMENTS=whole|split overrides.
+constexpr int kWholeSegmentKeys = 256;
+
+bool whole_segments(int num_seqs, int num_kv_heads, int max_seqlen_k) {
+    const bool fits = (long)num_seqs * num_kv_heads <= pkv::kDecodeWaves &&
+                      num_seqs <= pkv::kInlinePlanSeqs;
+    const char* e = std::getenv("PKV_DECODE_SEGMENTS");
+    if (e && !std::strcmp(e, "whole")) return fits;
+    if (e && !std::strcmp(e, "split")) return false;
+    return fits && max_seqlen_k <= kWholeSegmentKeys;
+}
+
 template <typename T, int D>
 int launch_prefill(const pkv::PrefillParams& pp, hipStream_t stream, const char* what) {
     const long tiles = prefill_tiles(pp);
@@ -247,6 +264,12 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
         hipLaunchKernelGGL((pkv::merge_kernel<T, D>), dim3((unsigned)((long)dp.Hq * num_seqs)),
                            dim3(64), 0, stream, mp);
         return hip_status("merge launch");
+    }
+    if (dp.whole_segments) {
+        // one wave per segment: nothing is cut, so no merge
+        hipLaunchKernelGGL((pkv::decode_kernel<T, D, false>),
+                           dim3((unsigned)((long)num_seqs * dp.Hkv)), dim3(64), 0, stream, dp);
+        return hip_status("decode launch");
     }
     if (dp.prefix_states)
         hipLaunchKernelGGL((pkv::decode_kernel<T, D, true>), dim3(pkv::kDecodeWaves), dim3(64), 0,
@@ -570,6 +593,9 @@ int attention_impl(void* out, const void* q, const void* k_pool, const void* v_p
                                  : launch_prefix_pass<float, 64>(cp, spp, sc, cpl.max_chunks > 1, st);
         if (rc) return rc;
     }
+    // decode-only steps whose segments are all short: one wave per segment
+    dp.whole_segments = (max_seqlen_q <= pl.wmax && !dp.prefix_states &&
+                         whole_segments(num_seqs, num_kv_heads, max_seqlen_k)) ? 1 : 0;
     if (dtype == PKV_BF16)
         rc = head_dim == 128 ? launch_attention<pkv::bf16_t, 128>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st)
                              : launch_attention<pkv::bf16_t, 64>(plp, dp, mp, pp, max_seqlen_q, total_q, num_seqs, st);

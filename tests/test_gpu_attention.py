@@ -89,6 +89,28 @@ def test_sharp_softmax_step(q_mul, dtype):
               tol_scale=q_mul if dtype == torch.float32 else 1.0)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_whole_segment_decode(G, dtype, monkeypatch):
+    """Decode steps run with one wave per (sequence, kv head) segment (no
+    segment cut, no merge launch; the library picks it for steps whose
+    segments are all short), forced here on longer ones too: page-edge
+    contexts, verify windows and a left-padded step against the oracle."""
+    monkeypatch.setenv("PKV_DECODE_SEGMENTS", "whole")
+    log(f"whole-segment decode G={G} {dtype}")
+    st = W.build_step("whole-decode", EDGE_LENS, [1] * len(EDGE_LENS), 2 * G, 2, 128, dtype,
+                      310 + G)
+    _run_full(st, f"whole-segment decode G={G}")
+    W_ = max(1, 16 // G)
+    ql = [min(W_, L, 1 + i % W_) for i, L in enumerate(WINDOW_LENS)]
+    st = W.build_step("whole-windows", WINDOW_LENS, ql, 2 * G, 2, 64, dtype, 320 + G)
+    _run_full(st, f"whole-segment windows G={G}")
+    st = W.build_step("whole-padded", [300, 2000, 1000, 17], [1, 1, 1, 1], 2 * G, 2, 128, dtype,
+                      330 + G, padded=True)
+    _run_full(st, f"whole-segment left-padded G={G}")
+
+
 WINDOW_LENS = [2, 15, 16, 17, 31, 33, 64, 65, 100, 257, 1000, 1600]
 
 
