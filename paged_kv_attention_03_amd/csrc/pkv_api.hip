@@ -193,9 +193,13 @@ bool prefill_long(const pkv::PrefillParams& pp) {
 
 // Whether a step with prefill sequences runs as one launch (step_kernel:
 // decode waves, then prefill tiles, in one grid) or as separate decode and
-// prefill launches.  The environment variable PKV_MIXED_STEP=fused|split
-// overrides the default.
-constexpr bool kFusedStepDefault = false;
+// prefill launches.  One launch, measured on MI355X per attention call
+// (alternating runs, caches cleared before each step): the mixed
+// chunked-prefill step 0.1366 against 0.1411 ms, 64 decodes + two 512-token
+// chunks 0.294 against 0.311, 128 decodes + four 256-token chunks 0.370
+// against 0.392, 8 decodes + one 2048-token chunk 0.2667 against 0.2693.
+// The environment variable PKV_MIXED_STEP=fused|split overrides the default.
+constexpr bool kFusedStepDefault = true;
 
 bool fused_step() {
     const char* e = std::getenv("PKV_MIXED_STEP");
