@@ -6,7 +6,7 @@ context, mixed steps, left-padded steps; plus bitwise
 properties of the GPU path itself (physical page placement, run-to-run
 determinism, shared versus duplicated prefix pages) and a large packed step
 checked on sampled tokens; a step with 8x and 16x queries (sharp softmax rows)
-pins the logit precision.  Pools are NaN outside the valid rows."""
+pins the logit precision; sequences with no query token in the step.  Pools are NaN outside the valid rows."""
 import numpy as np
 import pytest
 import torch
@@ -147,6 +147,31 @@ def test_windows_only_step(max_q, dtype):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("mixed", ["fused", "split"])
+def test_sequences_without_query_tokens(mixed, dtype, monkeypatch):
+    """Sequences that contribute no query token to the step (query_start_loc
+    repeats a value: the first, the last and runs in between) sit among
+    decodes, verify windows and prefill chunks; they own no output row, and
+    the tokens around them keep their rows and keys.  Both launch forms of a
+    mixed step, then a decode-only step in both decode forms."""
+    monkeypatch.setenv("PKV_MIXED_STEP", mixed)
+    lens = [40, 300, 17, 900, 64, 64, 2000, 33, 1500, 5]
+    ql = [0, 1, 0, 3, 0, 0, 700, 0, 40, 0]
+    log(f"zero-token sequences {mixed} {dtype} q_lens={ql}")
+    st = W.build_step("zero-q-mixed", lens, ql, 8, 2, 128, dtype, 910)
+    qsl = st.query_start_loc()
+    assert list(qsl).count(0) == 2 and qsl[-1] == st.total_q
+    _run_full(st, f"zero-token sequences, mixed step ({mixed})")
+    if mixed == "split":
+        for form in ("whole", "split"):
+            monkeypatch.setenv("PKV_DECODE_SEGMENTS", form)
+            st = W.build_step("zero-q-decode", [100, 17, 250, 64, 1, 200], [0, 1, 0, 1, 1, 0],
+                              16, 2, 64, dtype, 920)
+            _run_full(st, f"zero-token sequences, decode step ({form} segments)")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
 def test_left_padded_step_matches_oracle(dtype):
     lens = [5, 40, 33, 16, 700, 1300, 260]
     ql = [1, 2, 1, 16, 1, 100, 1]
@@ -229,6 +254,43 @@ def test_many_sequences(num_seqs, dtype):
     log(f"many sequences: {num_seqs} {dtype}")
     st = W.build_step("many-seqs", lens, ql, 16, 4, 64, dtype, 950 + num_seqs)
     _run_full(st, f"{num_seqs} sequences")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+def test_most_sequences_a_step_takes(dtype):
+    """16384 sequences, the most a step may hold (the plan kernel keeps one
+    count per sequence in LDS): short ragged contexts, decodes, 2-token
+    windows and sequences with no query token, against the oracle on every
+    output.  The pools are filled directly -- one seeded draw over every slot,
+    NaN wherever no sequence has a key -- rather than row by row through the
+    append kernel, which would take minutes of host time at this count."""
+    n = 16384
+    rng = np.random.default_rng(n)
+    lens = rng.integers(1, 48, size=n)
+    ql = [0 if i % 97 == 13 else (2 if (i % 11 == 4 and L >= 2) else 1)
+          for i, L in enumerate(lens.tolist())]
+    log(f"{n} sequences {dtype}")
+    st = W.build_step("max-seqs", lens.tolist(), ql, 8, 2, 64, dtype, 960)
+    assert st.num_seqs == n
+    md = st.metadata("cpu")
+    bt = md["block_tables"].numpy()
+    npg = (lens + 15) // 16
+    s_idx = np.repeat(np.arange(n), npg)
+    j_idx = np.concatenate([np.arange(k) for k in npg])
+    pages = bt[s_idx, j_idx]
+    assert np.unique(pages).size == pages.size
+    used = np.minimum(16, lens[s_idx] - 16 * j_idx)
+    valid = np.zeros((st.num_blocks, 16), dtype=bool)
+    valid[pages] = np.arange(16)[None, :] < used[:, None]
+    shape = (st.num_blocks, st.num_kv_heads, 16, st.head_dim)
+    hole = torch.from_numpy(~valid)[:, None, :, None].expand(shape)
+    kp = W.randn(shape, 961, "cpu", dtype).masked_fill(hole, float("nan"))
+    vp = W.randn(shape, 962, "cpu", dtype).masked_fill(hole, float("nan"))
+    q = st.make_q("cpu")
+    out = gpu_attention(st, q.cuda(), kp.cuda(), vp.cuda())
+    ref = oracle_step(st, q, pools=(kp, vp))
+    check_close(out, ref, st.dtype, f"{n} sequences")
 
 
 @pytest.mark.gpu
