@@ -292,7 +292,11 @@ template <typename T, int D>
 struct DecodeGeom {
     static constexpr int EB = Elem<T>::kBytes;
     static constexpr int RB = D * EB;                  // bytes per K/V row
-    static constexpr int RS = RB + 16;                 // LDS row stride (bank spread)
+    // LDS row stride of a staged V page.  bfloat16 pages are read by the
+    // transposing read (16 lanes take 8 bytes from each of 4 consecutive
+    // rows): a 32-byte pad puts those 4 rows on distinct banks.  float32
+    // pages are read 4 bytes per lane, for which 16 bytes spread the rows.
+    static constexpr int RS = RB + (EB == 2 ? 32 : 16);
     static constexpr int PAGE_LDS = kPage * RS;        // LDS bytes per staged V page
     static constexpr int NT = D / 16;                  // 16-wide d tiles of the output
     static constexpr int VCH = RB * kPage / 16 / kWave;  // 16-B chunks per lane per V page
@@ -699,11 +703,15 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
             }
             l_run += psum;
 
-            // O^T += V^T P^T, V^T gathered from the staged pages
+            // O^T += V^T P^T, V^T from the staged pages
             if constexpr (kBF) {
                 u32x4 pbv = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
                              pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
-                const uint16_t* l16 = reinterpret_cast<const uint16_t*>(lds_v);
+                // transposing reads: the 16 lanes of group grp point at keys
+                // 4 grp .. 4 grp + 3 of a page, 4 lanes per key and 8 bytes
+                // each over tile t's 16 columns, and lane col receives column
+                // 16 t + col of those 4 keys -- the keys its P^T entries hold
+                const uint8_t* vb = lds_v + (4 * grp + (col >> 2)) * Gm::RS + (col & 3) * 8;
                 uint32_t keep[4];
                 if constexpr (EDGE) {
 #pragma unroll
@@ -715,15 +723,12 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
                 }
 #pragma unroll
                 for (int t = 0; t < Gm::NT; ++t) {
-                    const int d = t * 16 + col;
-                    u32x4 a;
+                    const uint2 lo = lds_read_tr16(vb + t * 32);
+                    const uint2 hi = lds_read_tr16(vb + Gm::PAGE_LDS + t * 32);
+                    u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                    if constexpr (EDGE) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int x = q >> 1;
-                        const int k0 = grp * 4 + (q & 1) * 2;
-                        const int base = (x * Gm::PAGE_LDS + k0 * Gm::RS) / 2 + d;
-                        a[q] = (uint32_t)l16[base] | ((uint32_t)l16[base + Gm::RS / 2] << 16);
-                        if constexpr (EDGE) a[q] &= keep[q];
+                        for (int q = 0; q < 4; ++q) a[q] &= keep[q];
                     }
                     acc[t] = mfma_bf16(a, pbv, acc[t]);
                 }

@@ -81,6 +81,18 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) {
     *reinterpret_cast<u32x4*>(p) = v;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// (i % 4) of the 4 consecutive 16-bit values that lane 4r + i / 4 points at,
+// for r = 0..3 (so 16 lanes pointing at a 4 x 16 block of 16-bit values, 4
+// lanes per row, receive its 16 columns).
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* addr) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)addr);
+    return __builtin_bit_cast(uint2, v);
+}
+
 // Max / sum over the four lanes that share a column (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float col_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 16));

@@ -80,8 +80,6 @@ constexpr int kPrefillRowBlocks = 4;                 // 32-row blocks per workgr
 constexpr int kPrefillRows = 32 * kPrefillRowBlocks;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 // 16 bytes from global memory straight into LDS: lane l writes block + 16 * l
 // (block is wave-uniform; M0 holds its LDS address).  Written as inline
@@ -118,14 +116,6 @@ __device__ __forceinline__ void mfma_priority(int hi) {
     if (hi) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
-}
-
-// Transposing LDS read: within each 16-lane group, lane i receives element
-// (i % 4) of the 4 consecutive 16-bit values that lane 4r + i / 4 points at,
-// for r = 0..3.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* addr) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)addr);
-    return __builtin_bit_cast(uint2, v);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): a fence
