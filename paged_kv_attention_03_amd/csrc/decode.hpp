@@ -342,6 +342,16 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
     const int S = p.num_seqs;
     int pb = 0, pe = 0;       // plan-kernel mode: this wave's pieces
     int64_t u0 = 0, u1 = 0;   // inline mode: this wave's units [u0, u1)
+    // The waves of an XCD first touch the block table together, one cache
+    // line per lane (tables up to 1 MiB), while the step metadata is read, so
+    // that the block-id reads that follow the plan hit that XCD's L2 rather
+    // than HBM.  The value is kept only so that the load stays.
+    int bt_touch = 0;
+    {
+        const int local = p.whole_segments ? (w >> 3) : (w & (kDecodeWaves / kXcds - 1));
+        const int64_t idx = ((int64_t)local * kWave + lane) * 32;
+        if (idx < (int64_t)S * p.max_blocks) bt_touch = p.block_tables[idx];
+    }
     if (inl) {
         // page pairs of every sequence and their exclusive prefix, in LDS
         const int per = (S + kWave - 1) / kWave;
@@ -776,6 +786,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
             finish_piece();
         }
     }
+    asm volatile("" ::"v"(bt_touch));
 }
 
 #undef PKV_FIELD
