@@ -775,6 +775,13 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
 
         if (K > 0) {
             PairRegs<T, D> A, B;
+            // With one wave per segment the segment's queries load before its
+            // pages: loads complete in order, so queries loaded after the
+            // first two pairs hold the first products until both pairs have
+            // arrived, a pair's latency of a short segment.  Spread over the
+            // waves, where the first pages matter more than the first
+            // products, the pages go first.
+            if (p.whole_segments) begin_piece(0);
             issue(A);
             issue(B);
             for (int k = 0; k < K; k += 2) {
