@@ -352,7 +352,32 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
         const int64_t idx = ((int64_t)local * kWave + lane) * 32;
         if (idx < (int64_t)S * p.max_blocks) bt_touch = p.block_tables[idx];
     }
-    if (inl) {
+    // One wave per segment: the wave's segment, (sequence w % S, kv head
+    // w / S), is its whole range, so it needs that sequence's metadata only,
+    // not the plan over every sequence, and the first window of the
+    // sequence's block-table row loads beside that metadata rather than after
+    // it (pages 0 .. kWindowPages - 1; staged again past them as usual).  The
+    // pair prefix in LDS then holds this sequence's pairs alone.
+    int32_t spec_ids[kWindowPages / kWave];
+    int spec_seq = -1;
+    if (inl && p.whole_segments) {
+        const int g = w / S, s = w - g * S;
+        if (g >= p.Hkv) return;
+        const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
+#pragma unroll
+        for (int c = 0; c < kWindowPages / kWave; ++c) {
+            const int pg = c * kWave + lane;
+            spec_ids[c] = pg < p.max_blocks ? bt[pg] : 0;
+        }
+        const int c = __builtin_amdgcn_readfirstlane(decode_pairs(
+            p.qsl, p.seq_lens, p.kv_start, s, p.wmax, p.total_q, p.max_seqlen_k, p.max_blocks));
+        if (c == 0) return;
+        for (int i = lane; i <= S; i += kWave) lds_pref[i] = i <= s ? 0 : c;
+        wave_lds_fence();
+        u0 = (int64_t)g * c;
+        u1 = u0 + c;
+        spec_seq = s;
+    } else if (inl) {
         // page pairs of every sequence and their exclusive prefix, in LDS
         const int per = (S + kWave - 1) / kWave;
         const int s_lo = min(S, lane * per), s_hi = min(S, s_lo + per);
@@ -379,18 +404,9 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
         wave_lds_fence();
         if (w == 0)
             for (int s = lane; s <= S; s += kWave) p.pair_prefix[s] = lds_pref[s];
-        const int32_t P_S = __builtin_amdgcn_readfirstlane(lds_pref[S]);
-        if (p.whole_segments) {
-            const int g = w / S, s = w - (w / S) * S;
-            if (g >= p.Hkv) return;
-            u0 = segment_start(g, __builtin_amdgcn_readfirstlane(lds_pref[s]), P_S);
-            u1 = u0 + (__builtin_amdgcn_readfirstlane(lds_pref[s + 1]) -
-                       __builtin_amdgcn_readfirstlane(lds_pref[s]));
-        } else {
-            const int64_t U = (int64_t)p.Hkv * P_S;
-            u0 = wave_start(w, U);
-            u1 = wave_start(w + 1, U);
-        }
+        const int64_t U = (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(lds_pref[S]);
+        u0 = wave_start(w, U);
+        u1 = wave_start(w + 1, U);
         if (u0 >= u1) return;
     } else {
         pb = p.portion_begin[w];
@@ -428,6 +444,14 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
         asm volatile("" : "+s"(m));
         return (col * m) >> 16;
     };
+
+    if (spec_seq >= 0) {
+#pragma unroll
+        for (int c = 0; c < kWindowPages / kWave; ++c)
+            lds_bid[c * kWave + lane] =
+                (spec_ids[c] >= 0 && spec_ids[c] < p.num_blocks) ? spec_ids[c] : 0;
+        wave_lds_fence();
+    }
 
     for (int b0 = pb;;) {
         // ---- this batch's segment pieces (up to 64) into lds_port
@@ -487,7 +511,9 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int w, 
         int is = PKV_FIELD(s, 0), ig = PKV_FIELD(g, 0);
         int ifirst = PKV_FIELD(kv_lo, 0) / kPage;
         int iendpg = (PKV_FIELD(kv_hi, 0) + kPage - 1) / kPage;
-        int wstart = -1, wseq = -1;
+        // the block-id window in LDS: pages [wstart, wstart + kWindowPages)
+        // of sequence wseq's row (the speculative window of a whole segment)
+        int wstart = spec_seq >= 0 ? 0 : -1, wseq = spec_seq;
         bool idone = false;
 
         auto issue = [&](PairRegs<T, D>& R) {
