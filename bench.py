@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -165,10 +166,16 @@ def device_copy_gbs(nbytes: int = 1 << 31, reps: int = 5) -> float:
 
 
 def source_hash() -> str:
+    """Hash of the decode kernels' code: their sources with comments and
+    whitespace removed, so that a counter record outlives edits of comments
+    but not of code."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_attention_03_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_attention_03_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,19 +8,20 @@
 // compute-bound).  The kernels therefore stream whole KV pages with coalesced
 // 16-byte loads and keep everything else on chip.
 //
-// Work split (split-key, balanced): a one-workgroup plan kernel counts the
-// page pairs of every decode sequence and cuts the list of all
-// (kv head, sequence, page pair) units into kDecodeWaves equal contiguous
-// ranges.  One persistent wavefront streams each range, crossing from one
-// (sequence, kv head) segment to the next without leaving the kernel, so every
-// wave does the same number of page pairs whatever the length mix.  Wave
-// numbers count along each XCD, so an XCD streams one kv head's pages (or a
-// contiguous run of heads) and pages shared by several sequences are re-read
-// from its L2.  A segment
-// that lies inside one wave's range is finished there and written to the
-// output; a segment cut by a range boundary leaves at most two partial results
-// per wave, which a small merge kernel combines with the usual log-sum-exp
-// rescaling.
+// Work split (split-key, balanced): the page pairs of every decode sequence
+// are counted and the list of all (kv head, sequence, page pair) units is cut
+// into kDecodeWaves equal contiguous ranges -- by every wave for itself up to
+// kInlinePlanSeqs sequences, by a one-workgroup plan kernel beyond.  One
+// persistent wavefront streams each range, crossing from one (sequence, kv
+// head) segment to the next without leaving the kernel, so every wave does
+// the same number of page pairs whatever the length mix.  Wave numbers count
+// along each XCD, so an XCD streams one kv head's pages (or a contiguous run
+// of heads) and pages shared by several sequences are re-read from its L2.  A
+// segment that lies inside one wave's range is finished there and written to
+// the output; a segment cut by a range boundary leaves at most two partial
+// results per wave, which a small merge kernel combines with the usual
+// log-sum-exp rescaling.  Steps whose segments are all short run instead one
+// wave per segment: nothing is cut and no merge follows.
 //
 // Per page pair, the query rows that share kv head g -- the G heads of each of
 // the sequence's n query tokens, column = token * G + head, G * n <= 16 -- are
@@ -30,8 +31,9 @@
 //   O^T[d][head]  += V^T[d][key] * P^T[key][head]      (MFMA, d as rows)
 // K goes straight from global memory into the A-operand registers (each lane
 // reads 16-byte pieces of one key row, so every load instruction touches 16
-// rows x 64 contiguous bytes).  V is staged through LDS, because the PV
-// product needs it key-major per lane (a transpose).  The online softmax keeps
+// rows x 64 contiguous bytes).  V is staged through LDS and read back by the
+// transposing LDS read, because the PV product needs it key-major per lane
+// (a transpose).  The online softmax keeps
 // one running max and sum per column; the max over the four lane groups of a
 // column is a two-step wavefront shuffle.  Keys outside [kv_start, seq_len)
 // are masked by selection, and their V entries are zeroed before the product,
