@@ -844,8 +844,20 @@ template <typename T, int D>
 __global__ void __launch_bounds__(64) merge_kernel(MergeParams p) {
     constexpr bool kBF = !__is_same(T, float);
     constexpr int PER = D / kWave;  // output elements per lane (1 or 2)
-    const int h = blockIdx.x % p.Hq;
-    const int s = blockIdx.x / p.Hq;
+    int h, s;
+    if (p.Hkv % kXcds == 0) {
+        // Workgroup b runs on XCD b % 8: give it a (sequence, head) whose kv
+        // head that XCD's decode waves streamed (with the kv heads a multiple
+        // of the XCDs each XCD takes whole heads), so that the partials it
+        // reads can still sit in that XCD's L2 (back-to-back steps: ~1 us).
+        const int x = (int)(blockIdx.x % kXcds), k = (int)(blockIdx.x / kXcds);
+        const int per = p.Hq / kXcds;
+        s = k / per;
+        h = x * per + k % per;
+    } else {
+        h = blockIdx.x % p.Hq;
+        s = blockIdx.x / p.Hq;
+    }
     if (s >= p.num_seqs) return;
     const int64_t c = p.pair_prefix[s + 1] - p.pair_prefix[s];
     if (c <= 0) return;
