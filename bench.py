@@ -394,14 +394,21 @@ def extra_prefill(steps: int, warmup: int):
     (the two chunks as their own step) against the dense bf16 matrix peak."""
     mixed = W.config_step(3, poison=False)
     sm = Step(mixed, gen_device="cuda")
-    wall, attn, _, _ = time_steps(sm, steps, warmup, flush_bytes=1 << 30)
+    # The three forms are timed in the order default, fused, split, split,
+    # fused, default and each is averaged over its two passes, so that a drift
+    # of the clocks over the sequence (the first pass after the large batch
+    # runs slower) weighs on all three alike.
+    passes = {"default": [], "fused": [], "split": []}
+    for mode in ("default", "fused", "split", "split", "fused", "default"):
+        timed = lambda: time_steps(sm, steps, warmup, flush_bytes=1 << 30)
+        passes[mode].append(timed() if mode == "default" else with_mixed_step(mode, timed))
+    mean = lambda mode, i: float(np.mean([r[i] for r in passes[mode]]))
+    wall, attn = mean("default", 0), mean("default", 1)
     res = {"workload": mixed.name, "packed_step_tokens_per_s": mixed.total_q / wall,
            "step_ms": wall * 1e3, "attention_ms": attn * 1e3}
     for mode in ("fused", "split"):
-        mw, ma, _, _ = with_mixed_step(mode, lambda: time_steps(sm, steps, warmup,
-                                                                flush_bytes=1 << 30))
-        res[f"{mode}_step_ms"] = mw * 1e3
-        res[f"{mode}_attention_ms"] = ma * 1e3
+        res[f"{mode}_step_ms"] = mean(mode, 0) * 1e3
+        res[f"{mode}_attention_ms"] = mean(mode, 1) * 1e3
     log(f"mixed step: attention {attn * 1e3:.4f} ms (default), fused {res['fused_attention_ms']:.4f}"
         f" ms, split {res['split_attention_ms']:.4f} ms")
     del sm
