@@ -29,11 +29,14 @@
  *     every index they follow, so they never access memory outside the
  *     buffers whose sizes the host arguments describe.  pkv_check_metadata()
  *     and pkv_check_slots() validate host copies when a caller wants that.
- *   - Two environment variables, read at each pkv_attention call, choose
+ *   - Three environment variables, read at each pkv_attention call, choose
  *     between launch forms of the same computation (the defaults are the
  *     faster forms measured): PKV_MIXED_STEP=fused|split runs a step with
  *     prefill chunks as one launch or as separate decode and prefill launches
- *     (bitwise the same output); PKV_DECODE_SEGMENTS=whole|split runs a
+ *     (bitwise the same output); PKV_STEP_TILE_FIRST=0..4 sets how many of
+ *     every 4 workgroups of that one launch compute their prefill tile before
+ *     their decode waves rather than after (default 3; bitwise the same
+ *     output); PKV_DECODE_SEGMENTS=whole|split runs a
  *     decode-only step with one wave per (sequence, kv head) -- where the step
  *     has at most 1024 such segments and 512 sequences -- or spread evenly
  *     over the decode waves (the same result up to float32 summation order).

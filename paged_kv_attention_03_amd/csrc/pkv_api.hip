@@ -208,6 +208,23 @@ bool fused_step() {
     return kFusedStepDefault;
 }
 
+// Of every 4 workgroups of the single launch that carry decode waves and a
+// tile, how many run the tile first.  Measured on MI355X per attention call
+// (medians of six alternating runs, caches cleared before each step; 0, 2, 3
+// and 4 of 4): the mixed chunked-prefill step 0.1411 / 0.1353 / 0.1321 /
+// 0.1368 ms, 8 decodes + one 2048-token chunk 0.2349 / 0.2293 / 0.2283 /
+// 0.2280, 16 decodes + two 1024-token chunks 0.2423 / 0.2352 / 0.2354 /
+// 0.2350; decode-heavier steps (64 decodes + two 512-token chunks, 128 + four
+// 256-token chunks) within 0.3% either way.  PKV_STEP_TILE_FIRST=0..4
+// overrides (the output is bitwise the same for every value).
+constexpr int kStepTileFirstDefault = 3;
+
+int step_tile_first() {
+    const char* e = std::getenv("PKV_STEP_TILE_FIRST");
+    if (e && e[0] >= '0' && e[0] <= '4' && e[1] == 0) return e[0] - '0';
+    return kStepTileFirstDefault;
+}
+
 // Whether a decode-only step runs one wave per (sequence, kv head) segment
 // (no segment cut, no merge launch) instead of spreading the units evenly
 // over kDecodeWaves waves.  Chosen when every segment is short (the host
@@ -257,6 +274,7 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
         constexpr int kWaves = pkv::kStepWaves<T>;
         sp.decode_per_wg = (kWaves < 8 || sp.prefill_wgs >= 2 * pkv::kDecodeWaves / 8) ? 4 : 8;
         sp.decode_wgs = pkv::kDecodeWaves / sp.decode_per_wg;
+        sp.tile_first = step_tile_first();
         const unsigned grid = (unsigned)std::max(sp.prefill_wgs, sp.decode_wgs);
         if (prefill_long<T, D>(pp))
             hipLaunchKernelGGL((pkv::step_kernel<T, D, true>), dim3(grid),

@@ -12,7 +12,10 @@
 // of the prefill ring), then the whole workgroup computes its prefill tile.
 // There is no grid-wide wait between the phases: a workgroup starts its tile
 // while others still decode, and workgroups without a tile leave their compute
-// unit to the tiles queued behind them.  Each decode wave and each tile does
+// unit to the tiles queued behind them.  Most workgroups that carry both run
+// their tile first and their decode waves after it, the rest the other way
+// round, so that the decode streams are spread over the launch instead of
+// all competing for HBM at its start while the matrix cores idle.  Each decode wave and each tile does
 // the same work, in the same order, as in the separate kernels, so the output
 // is bitwise the same; the merge of cut decode segments stays a launch of its
 // own after this one.
@@ -29,6 +32,8 @@ struct StepParams {
     int decode_wgs;     // workgroups [0, decode_wgs) run decode waves ...
     int decode_per_wg;  // ... in their first decode_per_wg waves
     int prefill_wgs;    // workgroups [0, prefill_wgs) then run their prefill tile
+    int tile_first;     // of every 4 workgroups of an XCD that carry both, this
+                        // many run their tile first and their decode waves after
 };
 
 // Decode waves per workgroup and the workgroups that carry them, so that
@@ -48,12 +53,22 @@ __global__ void __launch_bounds__(kPrefillThreads<T>) step_kernel(StepParams sp)
     __shared__ __attribute__((aligned(1024))) uint8_t lds[step_lds_bytes<T, D, LONG>()];
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int b = (int)blockIdx.x;
-    if (b < sp.decode_wgs && wave < sp.decode_per_wg) {
-        // the decode wave numbers of XCD b % 8 stay one contiguous range, as
-        // in the separate decode kernel (workgroups go to the XCDs in turn)
-        const int w = (b % kXcds) * (kDecodeWaves / kXcds) + (b / kXcds) * sp.decode_per_wg + wave;
-        decode_wave<T, D, false>(sp.dp, w, reinterpret_cast<DecodeLds<T, D>*>(lds)[wave]);
+    auto decode_part = [&]() {
+        if (b < sp.decode_wgs && wave < sp.decode_per_wg) {
+            // the decode wave numbers of XCD b % 8 stay one contiguous range, as
+            // in the separate decode kernel (workgroups go to the XCDs in turn)
+            const int w = (b % kXcds) * (kDecodeWaves / kXcds) + (b / kXcds) * sp.decode_per_wg + wave;
+            decode_wave<T, D, false>(sp.dp, w, reinterpret_cast<DecodeLds<T, D>*>(lds)[wave]);
+        }
+    };
+    // uniform over the workgroup
+    if (b < sp.prefill_wgs && b < sp.decode_wgs && ((b / kXcds) & 3) < sp.tile_first) {
+        prefill_tile<T, D, LONG>(sp.pp, b, *reinterpret_cast<PrefillLds<T, D, LONG>*>(lds));
+        __syncthreads();  // the tile is done with the LDS
+        decode_part();
+        return;
     }
+    decode_part();
     if (b >= sp.prefill_wgs) return;  // uniform over the workgroup
     __syncthreads();                  // the decode waves are done with the LDS
     prefill_tile<T, D, LONG>(sp.pp, b, *reinterpret_cast<PrefillLds<T, D, LONG>*>(lds));

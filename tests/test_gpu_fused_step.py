@@ -2,9 +2,12 @@
 against the separate launches and the float64 oracle.
 
 PKV_MIXED_STEP selects the path per call (fused: one launch for decode and
-prefill, then the merge; split: decode, merge, prefill).  Each decode wave and
-each prefill tile does the same work in both, so outputs must be bitwise
-equal; the fused output is also checked against the oracle.  Cases: the
+prefill, then the merge; split: decode, merge, prefill), PKV_STEP_TILE_FIRST
+how many of every 4 workgroups of the one launch compute their tile before
+their decode waves.  Each decode wave and each prefill tile does the same work
+in every form, so outputs must be bitwise equal (the fused launch is checked
+with the default order, every workgroup decode-first and every workgroup
+tile-first); the fused output is also checked against the oracle.  Cases: the
 mixed chunked-prefill workload in bf16 and its fp32 shadow, decodes with
 verify windows and chunks at several group sizes and head dims, a step past
 512 sequences (the plan kernel feeds the decode waves), contexts past 65,536
@@ -21,16 +24,20 @@ from tests.gpu_helpers import check_close, gpu_attention, gpu_pools, log, raw_bi
 from tests.helpers import oracle_pools, oracle_step
 
 
-def _with_mode(mode, fn):
-    old = os.environ.get("PKV_MIXED_STEP")
-    os.environ["PKV_MIXED_STEP"] = mode
+def _with_env(name, value, fn):
+    old = os.environ.get(name)
+    os.environ[name] = value
     try:
         return fn()
     finally:
         if old is None:
-            del os.environ["PKV_MIXED_STEP"]
+            del os.environ[name]
         else:
-            os.environ["PKV_MIXED_STEP"] = old
+            os.environ[name] = old
+
+
+def _with_mode(mode, fn):
+    return _with_env("PKV_MIXED_STEP", mode, fn)
 
 
 def _check(st, what):
@@ -42,6 +49,11 @@ def _check(st, what):
     split = _with_mode("split", lambda: gpu_attention(st, qd, kp, vp))
     fused = _with_mode("fused", lambda: gpu_attention(st, qd, kp, vp))
     assert np.array_equal(raw_bits(fused), raw_bits(split)), f"{what}: fused != split"
+    for order in ("0", "4"):
+        other = _with_env("PKV_STEP_TILE_FIRST", order,
+                          lambda: _with_mode("fused", lambda: gpu_attention(st, qd, kp, vp)))
+        assert np.array_equal(raw_bits(other), raw_bits(split)), \
+            f"{what}: fused with PKV_STEP_TILE_FIRST={order} != split"
     ref = oracle_step(st, q, pools=oracle_pools(st))
     check_close(fused, ref, st.dtype, f"{what} fused vs oracle")
 
