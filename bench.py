@@ -571,7 +571,7 @@ def bench_single(k, args):
                      "algorithmic_bytes_per_launch": kvb},
     }
     if k == 3:
-        # the same step with one launch (decode waves, then prefill tiles, in
+        # the same step with one launch (decode waves and prefill tiles in
         # one grid) and with separate launches
         modes = {}
         for mode in ("fused", "split"):

@@ -192,7 +192,7 @@ bool prefill_long(const pkv::PrefillParams& pp) {
 }
 
 // Whether a step with prefill sequences runs as one launch (step_kernel:
-// decode waves, then prefill tiles, in one grid) or as separate decode and
+// decode waves and prefill tiles in one grid) or as separate decode and
 // prefill launches.  One launch, measured on MI355X per attention call
 // (alternating runs, caches cleared before each step): the mixed
 // chunked-prefill step 0.1366 against 0.1411 ms, 64 decodes + two 512-token
@@ -266,7 +266,7 @@ int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
         if (int rc = hip_status("decode plan launch")) return rc;
     }
     if (max_seqlen_q > pl.wmax && !dp.prefix_states && fused_step()) {
-        // one launch: every workgroup runs its decode waves, then its tile
+        // one launch: every workgroup runs its decode waves and its tile
         pkv::StepParams sp;
         sp.dp = dp;
         sp.pp = pp;

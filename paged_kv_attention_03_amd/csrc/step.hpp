@@ -9,13 +9,13 @@
 // and a decode wave needs ~250 VGPRs of its own.  So the single launch runs
 // them in phases inside each workgroup: its first waves stream decode units
 // (exactly the waves of the separate decode kernel, with their LDS carved out
-// of the prefill ring), then the whole workgroup computes its prefill tile.
-// There is no grid-wide wait between the phases: a workgroup starts its tile
-// while others still decode, and workgroups without a tile leave their compute
-// unit to the tiles queued behind them.  Most workgroups that carry both run
-// their tile first and their decode waves after it, the rest the other way
-// round, so that the decode streams are spread over the launch instead of
-// all competing for HBM at its start while the matrix cores idle.  Each decode wave and each tile does
+// of the prefill ring), and the whole workgroup computes its prefill tile.
+// Most workgroups that carry both run their tile first and their decode waves
+// after it, the rest the other way round, so that the decode streams are
+// spread over the launch instead of all competing for HBM at its start while
+// the matrix cores idle.  There is no grid-wide wait between the phases, and
+// workgroups without a tile leave their compute unit to the tiles queued
+// behind them.  Each decode wave and each tile does
 // the same work, in the same order, as in the separate kernels, so the output
 // is bitwise the same; the merge of cut decode segments stays a launch of its
 // own after this one.
