@@ -35,7 +35,7 @@
  *     prefill chunks as one launch or as separate decode and prefill launches
  *     (bitwise the same output); PKV_STEP_TILE_FIRST=0..4 sets how many of
  *     every 4 workgroups of that one launch compute their prefill tile before
- *     their decode waves rather than after (default 3; bitwise the same
+ *     their decode waves rather than after (default 2; bitwise the same
  *     output); PKV_DECODE_SEGMENTS=whole|split runs a
  *     decode-only step with one wave per (sequence, kv head) -- where the step
  *     has at most 1024 such segments and 512 sequences -- or spread evenly

@@ -210,14 +210,14 @@ bool fused_step() {
 
 // Of every 4 workgroups of the single launch that carry decode waves and a
 // tile, how many run the tile first.  Measured on MI355X per attention call
-// (medians of six alternating runs, caches cleared before each step; 0, 2, 3
-// and 4 of 4): the mixed chunked-prefill step 0.1411 / 0.1353 / 0.1321 /
-// 0.1368 ms, 8 decodes + one 2048-token chunk 0.2349 / 0.2293 / 0.2283 /
-// 0.2280, 16 decodes + two 1024-token chunks 0.2423 / 0.2352 / 0.2354 /
-// 0.2350; decode-heavier steps (64 decodes + two 512-token chunks, 128 + four
-// 256-token chunks) within 0.3% either way.  PKV_STEP_TILE_FIRST=0..4
-// overrides (the output is bitwise the same for every value).
-constexpr int kStepTileFirstDefault = 3;
+// (medians of six alternating runs, caches cleared before each step; 0 to 4
+// of 4): the mixed chunked-prefill step 0.1366 / 0.1321 / 0.1315 / 0.1369 /
+// 0.1440 ms, 64 decodes + two 512-token chunks 0.2735 / 0.2704 / 0.2643 /
+// 0.2754 / 0.2960, 8 decodes + one 2048-token chunk 0.2215 / 0.2172 / 0.2170
+// / 0.2209 / 0.2266, 16 decodes + two 1024-token chunks 0.2248 / 0.2177 /
+// 0.2182 / 0.2257 / 0.2330.  PKV_STEP_TILE_FIRST=0..4 overrides (the output
+// is bitwise the same for every value).
+constexpr int kStepTileFirstDefault = 2;
 
 int step_tile_first() {
     const char* e = std::getenv("PKV_STEP_TILE_FIRST");

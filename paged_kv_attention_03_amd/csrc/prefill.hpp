@@ -30,8 +30,11 @@
 // lane 4 consecutive keys of one column.  A wavefront issues at most one
 // instruction per 4-cycle turn of its SIMD, so the transfer bookkeeping is
 // kept to a few scalar instructions per stage (pre-scaled page offsets in LDS,
-// scalar-base loads).  The sequence that owns a tile is found by a binary
-// search over query_start_loc ("Replacing attention, reusing the rest": each
+// scalar-base loads).  The sequence that owns a tile is found from
+// query_start_loc: up to kPrefillCompactSeqs sequences by a prefix sum of
+// their tile counts that every wavefront computes (tiles numbered over the
+// prefill sequences only, the last tile first), beyond that by a binary
+// search over tile slots ("Replacing attention, reusing the rest": each
 // threadgroup finds its request by binary search over cu_seqlens).
 #pragma once
 
@@ -76,6 +79,9 @@ struct PrefillParams {
     int sp_tiles;  // state pass: tiles per sequence (grid = num_seqs x sp_tiles x Hkv)
 };
 
+constexpr int kPrefillCompactSeqs = 512;  // up to this many sequences in a step,
+                                         // tiles are numbered over the prefill
+                                         // sequences only
 constexpr int kPrefillRowBlocks = 4;                 // 32-row blocks per workgroup
 constexpr int kPrefillRows = 32 * kPrefillRowBlocks;
 
@@ -248,25 +254,77 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, const int b
     const int bid = (int)((unsigned)block / (unsigned)p.Hkv);
     const int BQ = p.tile_tokens;
 
-    // ---- which sequence owns this tile: largest s with qsl[s]/BQ + s <= bid
-    // (the state pass: sp_tiles tiles per sequence, in order)
+    // ---- which sequence owns this tile, and which of its tiles it is
     const bool SP = p.state != nullptr;  // shared-prefix state pass
-    int lo = 0, hi = p.num_seqs - 1;
+    int s = 0, qt = 0;
     if (SP) {
-        lo = bid / p.sp_tiles;
-        if (lo >= p.num_seqs) return;
+        // the state pass: sp_tiles tiles per sequence, in order
+        s = bid / p.sp_tiles;
+        if (s >= p.num_seqs) return;
+        qt = bid - s * p.sp_tiles;
+    } else if (p.num_seqs <= kPrefillCompactSeqs) {
+        // Tiles numbered over the prefill sequences only (decode sequences
+        // take none), from one read of the query offsets by every wavefront
+        // (the result is uniform): the workgroups with a tile are then the
+        // first ones, which start first, and none waits behind a workgroup
+        // that had nothing to do.  The last tile comes first -- within a
+        // chunk the later tiles see more keys -- so that when there are more
+        // tiles than compute units the longest start first.
+        const int S = p.num_seqs;
+        const int per = (S + kWave - 1) / kWave;
+        const int s_lo = min(S, lane * per), s_hi = min(S, s_lo + per);
+        auto tiles_of = [&](int t) {
+            const int a = p.qsl[t];
+            int m = p.qsl[t + 1] - a;
+            if (a < 0 || a >= p.total_q || m < max(2, p.min_q)) return 0;
+            if (m > p.total_q - a) m = (int)(p.total_q - a);
+            return (m + BQ - 1) / BQ;
+        };
+        int own = 0;
+        for (int t = s_lo; t < s_hi; ++t) own += tiles_of(t);
+        int incl = own;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        const int c = total - 1 - bid;
+        if (c < 0) return;  // uniform: no tile left for this workgroup
+        const int excl = incl - own;
+        const bool holder = c >= excl && c < incl;
+        int hs = 0, hq = 0;
+        if (holder) {
+            int run = excl;
+            for (int t = s_lo; t < s_hi; ++t) {
+                const int k = tiles_of(t);
+                if (c < run + k) {
+                    hs = t;
+                    hq = c - run;
+                    break;
+                }
+                run += k;
+            }
+        }
+        const int src = __ffsll((unsigned long long)__ballot(holder)) - 1;
+        s = __builtin_amdgcn_readlane(hs, src);
+        qt = __builtin_amdgcn_readlane(hq, src);
     } else {
+        // beyond that many sequences: tile slot bid of the sequence with the
+        // largest s such that qsl[s] / BQ + s <= bid (slots of decode
+        // sequences and of the rounding stay empty)
+        int lo = 0, hi = p.num_seqs - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (p.qsl[mid] / BQ + mid <= bid) lo = mid; else hi = mid - 1;
         }
+        s = lo;
+        qt = bid - (p.qsl[s] / BQ + s);
     }
-    const int s = lo;
     int q0 = p.qsl[s];
     int n = p.qsl[s + 1] - q0;
     if (q0 < 0 || q0 >= p.total_q || n < (SP ? 1 : max(2, p.min_q))) return;
     if (n > p.total_q - q0) n = (int)(p.total_q - q0);
-    const int qt = SP ? bid - s * p.sp_tiles : bid - (q0 / BQ + s);
     const int tok0 = qt * BQ;
     if (qt < 0 || tok0 >= n) return;
     const int ntok = min(BQ, n - tok0);

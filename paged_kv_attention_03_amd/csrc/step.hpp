@@ -10,8 +10,8 @@
 // them in phases inside each workgroup: its first waves stream decode units
 // (exactly the waves of the separate decode kernel, with their LDS carved out
 // of the prefill ring), and the whole workgroup computes its prefill tile.
-// Most workgroups that carry both run their tile first and their decode waves
-// after it, the rest the other way round, so that the decode streams are
+// Half the workgroups that carry both run their tile first and their decode
+// waves after it, the rest the other way round, so that the decode streams are
 // spread over the launch instead of all competing for HBM at its start while
 // the matrix cores idle.  There is no grid-wide wait between the phases, and
 // workgroups without a tile leave their compute unit to the tiles queued
