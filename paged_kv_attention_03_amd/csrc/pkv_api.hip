@@ -259,6 +259,15 @@ template <typename T, int D>
 int launch_attention(const pkv::PlanParams& pl, const pkv::DecodeParams& dp,
                      const pkv::MergeParams& mp, const pkv::PrefillParams& pp, int max_seqlen_q,
                      int64_t total_q, int num_seqs, hipStream_t stream) {
+    // A step whose host bounds leave no room for a sequence of the decode path
+    // runs the prefill launch alone, without a decode pass and a merge that
+    // would find nothing to do.  Every sequence has at most max_seqlen_q query
+    // tokens and they add up to total_q, so d sequences of at most wmax tokens
+    // need num_seqs * max_seqlen_q - total_q >= d * (max_seqlen_q - wmax): a
+    // smaller slack means d = 0 (steps of equal-length prefill chunks, for one).
+    if (max_seqlen_q > pl.wmax && !dp.prefix_states &&
+        (int64_t)num_seqs * max_seqlen_q - total_q < (int64_t)(max_seqlen_q - pl.wmax))
+        return launch_prefill<T, D>(pp, stream, "prefill launch");
     // sequences with up to pl.wmax query tokens: plan (large batches only;
     // otherwise each decode wave plans its own pieces), split-key pass, merge
     if (!dp.inline_plan) {

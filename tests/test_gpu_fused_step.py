@@ -71,7 +71,11 @@ CASES = [
     ("g8-d64", [5000, 17, 4100, 260], [1, 1, 300, 2], 32, 4, 64, torch.bfloat16),
     ("g1-f32-d64", [400, 1000, 31, 150], [1, 60, 1, 149], 4, 4, 64, torch.float32),
     ("g5-f32-d128", [700, 2048, 64], [1, 512, 3], 40, 8, 128, torch.float32),
+    # equal chunks: the host bounds rule out decodes, so the prefill launch runs alone
     ("prefill-only", [3000, 1024], [1024, 1024], 32, 8, 128, torch.bfloat16),
+    # chunks whose bounds leave room for decodes that are not there: the one
+    # launch's decode waves find nothing
+    ("prefill-only-loose", [3000, 1024, 300], [1024, 6, 6], 32, 8, 128, torch.bfloat16),
     ("g16-chunk", [1200, 90, 3000], [1, 1, 33], 16, 1, 128, torch.bfloat16),
 ]
 
