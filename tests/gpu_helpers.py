@@ -2,6 +2,8 @@
 (via the Python binding) and compare with the float64 oracle.  Test code."""
 import math
 
+import os
+
 import numpy as np
 import torch
 
@@ -67,6 +69,39 @@ def oracle_seq_outputs(st, q_host, seqs, gen_device="cpu", tokens=None):
                                                     [0, 1], st.scale))
             res[s] = np.concatenate(outs)
     return res
+
+
+def oracle_seq_blocks(st, q_host, s, block=500, gen_device="cpu"):
+    """Oracle outputs of every query token of sequence ``s``, computed in
+    blocks of ``block`` tokens on a thread pool: tokens [i0, i1) of an n-token
+    chunk over L keys are exactly the (i1 - i0)-token chunk at the end of the
+    first L - n + i1 keys, so each block is one oracle call of its own (the
+    oracle's own threads split a call by (sequence, kv head) only, which
+    leaves most cores idle on one long sequence).  Returns float64 [n, Hq, D]."""
+    from concurrent.futures import ThreadPoolExecutor
+    qsl = st.query_start_loc()
+    k, v = st.seq_kv(s, gen_device)
+    k, v = k.cpu(), v.cpu()
+    L = k.shape[0]
+    bs = 16
+    nb = max(1, (L + bs - 1) // bs)
+    kp = torch.full((nb, st.num_kv_heads, bs, st.head_dim), float("nan"), dtype=st.dtype)
+    vp = kp.clone()
+    kp, vp = oracle.oracle_append(kp, vp, k, v, np.arange(L, dtype=np.int64))
+    bt = np.arange(nb, dtype=np.int32)[None]
+    qrows = q_host[qsl[s]:qsl[s + 1]]
+    n = qrows.shape[0]
+    cuts = list(range(0, n, block)) + [n]
+
+    def run(j):
+        i0, i1 = cuts[j], cuts[j + 1]
+        return oracle.oracle_attention(qrows[i0:i1], kp, vp, bt, [L - n + i1], [0, i1 - i0],
+                                       st.scale, threads=1)
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        parts = list(pool.map(run, range(len(cuts) - 1)))
+    return np.concatenate(parts)
 
 
 def contiguous_pool(rows, num_kv_heads, head_dim, dtype, bs=16):
