@@ -12,8 +12,9 @@
  *    that was reserved once, addressed through a slot per token (slot =
  *    physical page * page_size + offset in page; a negative slot means "skip").
  *    Sources: vllm-metal v0.4.0 release post, "Set a predictable memory budget"
- *    (one pool reserved at startup serves every request) and "Prefix caching on
- *    hybrid models" (rows are written in place instead of copying the pool).
+ *    (one pool reserved at startup serves every request) and "Replacing
+ *    attention, reusing the rest" (keys and values stay in fixed-size pages,
+ *    so a request grows by filling its pages, without reshaping a cache).
  *
  *  - Attention.  One engine step packs the query tokens of many sequences on one
  *    token axis, with query_start_loc (cu_seqlens) marking where each sequence's
