@@ -134,7 +134,10 @@ size_t pkv_attention_workspace_size(int num_seqs, int64_t total_q, int max_seqle
  *
  * Host bounds: max_seqlen_q >= every sequence's query count, max_seqlen_k >=
  * every seq_lens[s]; both size the launch grids.  total_q = query_start_loc
- * [num_seqs].  With G = num_q_heads / num_kv_heads and
+ * [num_seqs], so total_q <= num_seqs * max_seqlen_q (else PKV_E_ARG); when the
+ * bounds leave no room for a sequence of W or fewer query tokens
+ * (num_seqs * max_seqlen_q - total_q < max_seqlen_q - W), only the prefill
+ * kernel is launched.  With G = num_q_heads / num_kv_heads and
  * W = min(16 / G, max_seqlen_q) (integer division), sequences with 1..W query
  * tokens -- decodes, and speculative-verify windows of a few draft tokens --
  * take the split-key decode path; sequences with more take the chunked-prefill

@@ -434,6 +434,10 @@ int attention_impl(void* out, const void* q, const void* k_pool, const void* v_p
         return fail(PKV_E_ARG, "max_seqlen_k %d exceeds the block-table width (%d pages of %d)",
                     max_seqlen_k, max_blocks_per_seq, block_size);
     if (total_q > 0x7fffffffLL) return fail(PKV_E_ARG, "total_q too large");
+    // the query counts are at most max_seqlen_q each and add up to total_q
+    if (total_q > (int64_t)num_seqs * max_seqlen_q)
+        return fail(PKV_E_ARG, "total_q %lld exceeds num_seqs %d x max_seqlen_q %d",
+                    (long long)total_q, num_seqs, max_seqlen_q);
     if (!std::isfinite(scale) || !(scale > 0.f))
         return fail(PKV_E_ARG, "scale %g is not finite and positive", (double)scale);
     const size_t eb = elem_bytes(dtype);

@@ -59,6 +59,7 @@ def _attn(lib, **over):
     (dict(msk=8 * 16 + 1), pkv.PKV_E_ARG),           # wider than the block table
     (dict(msq=200), pkv.PKV_E_ARG),                  # more queries than keys
     (dict(msq=0), pkv.PKV_E_ARG),
+    (dict(total_q=5), pkv.PKV_E_ARG),                # 5 query tokens over 4 sequences of at most 1
     (dict(nb=0), pkv.PKV_E_ARG),
     (dict(num_seqs=-1), pkv.PKV_E_ARG),
     (dict(scale=float("nan")), pkv.PKV_E_ARG),
